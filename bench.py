@@ -1,0 +1,256 @@
+"""Benchmark: grouped routed-MoE prefill on one GPU.
+
+One step = the whole path on one batch: route build (histogram, prefix,
+scatter), grouped FFN (schedule, gate/up GEMM + SwiGLU, down GEMM) and the
+route-weighted combine, with every input already resident in HBM.  The
+default workload is the 401-token prefill: d=4096, f=2048, 256 experts, top-6,
+bf16, 5% of routes masked.
+
+Printed: one JSON line with whole-path tokens/s, the dominant kernel's
+roofline fraction (gate/up stage, timed with HIP events on the launch stream
+inside the timed region) and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+METRIC = "routed-MoE prefill tokens/s + % of MFMA/HBM roofline at T=401/2048/8192"
+KERNEL_SOURCES = ["routed_expert_prefill_amd/csrc/ffn_bf16.hip",
+                  "routed_expert_prefill_amd/csrc/ffn_fp8.hip",
+                  "routed_expert_prefill_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl, counts, T):
+    """Bytes and flops the method must move/compute, from the realized histogram.
+
+    counts: active rows per expert.  Each stage's bytes are what it must read
+    and write once (weights of the experts that received rows, activations,
+    h, y, route metadata); the dense all-experts work the method avoids is not
+    counted.  Returns per-stage and whole-path totals.
+    """
+    d, f, k = wl.d, wl.f, wl.k
+    R = T * k
+    R_act = int(sum(counts))
+    used = sum(1 for c in counts if c > 0)
+    fp8 = wl.dtype == "fp8"
+    wb = 1 if fp8 else 2
+    sc = 4 * (f // 128) * (d // 128) if fp8 else 0  # one scale grid (bytes)
+    st = {}
+    st["route"] = 30 * R  # ids, mask, gates read; permutations written and re-read
+    if fp8:
+        st["plan"] = T * d * 2 + T * d + 4 * T  # x read, codes and scales written
+        st["gate_up"] = used * 2 * (f * d + sc) + T * d + 4 * T + 4 * R_act + R_act * f * 2
+        st["down"] = (R_act * f * 2 + R_act * f + 4 * R_act  # h quantised per row
+                      + used * (d * f + sc) + R_act * f + 4 * R_act + R_act * d * 4)
+    else:
+        st["plan"] = 0
+        st["gate_up"] = used * 2 * f * d * wb + T * d * 2 + 4 * R_act + R_act * f * 2
+        st["down"] = used * d * f * wb + R_act * f * 2 + R_act * d * 4
+    st["combine"] = R_act * d * 4 + T * d * 4
+    return {"R_act": R_act, "experts_used": used, "stage_bytes": st,
+            "gate_up_bytes": st["gate_up"], "gate_up_flops": 4.0 * d * f * R_act,
+            "path_bytes": sum(st.values()), "path_flops": 6.0 * d * f * R_act}
+
+
+def traffic_from_profiles(workload: str):
+    """HBM traffic of the gate/up stage from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"gate_up_traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, r, n_experts: int):
+    """The fp64 oracle (expert-major, BLAS) on a bounded sample of the workload:
+    the fixed part (route table, combine) on all routes plus n_experts experts'
+    FFNs, extrapolated to all active experts."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import moe as omoe
+    from oracle.route import route_table
+    from routed_expert_prefill_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    fp8 = wl.dtype == "fp8"
+    rt = route_table(r.topk_ids, r.route_mask, wl.E)
+    active = [e for e in range(wl.E) if rt.counts[e] > 0]
+    subset = active[:max(1, min(n_experts, len(active)))]
+    cache = {e: synth.expert_weights(wl, e, 0) for e in subset}
+    src = cache.__getitem__
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, src, wl.E, fp8=fp8, expert_subset=[])
+        t_fixed = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, src, wl.E, fp8=fp8, expert_subset=subset)
+        t_sub = time.perf_counter() - t0
+    per_expert = max(t_sub - t_fixed, 0.0) / len(subset)
+    t_total = t_fixed + per_expert * len(active)
+    blas = [i.get("internal_api") for i in threadpool_info()]
+    _ = np
+    return {
+        "value": round(wl.T / t_total, 3),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"moe_ref_blocked (fp64, BLAS {','.join(b for b in blas if b)}) on all {wl.T} tokens' "
+                   f"route table and combine plus the FFN of {len(subset)} of {len(active)} active experts "
+                   f"({t_sub:.1f} s measured, fixed part {t_fixed:.2f} s), extrapolated to all active experts"),
+        "seconds_extrapolated": round(t_total, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-experts", type=int, default=32, help="experts in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single GPU and has no "
+              "multi-GPU path (sharding across GPUs is a design note, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routed_expert_prefill_amd as rep
+    from routed_expert_prefill_amd import synth
+
+    name = args.workload or synth.DEFAULT_BENCH_WORKLOAD
+    wl = synth.WORKLOADS[name]
+    fp8 = wl.dtype == "fp8"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} CUs={props.multi_processor_count} "
+        f"arch={getattr(props, 'gcnArchName', '?')} mem={props.total_memory / 2**30:.0f} GiB")
+    rep.load_library()
+
+    t0 = time.perf_counter()
+    r, ten = synth.device_inputs(wl, seed=0, device=dev)
+    log(f"inputs for {name} generated and resident in HBM in {time.perf_counter() - t0:.1f} s")
+
+    run = rep.MoEPrefill(wl.T, wl.k, wl.E, wl.d, wl.f, fp8=fp8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    wargs = (ten["x"], ten["topk_ids"], ten["topk_w"], ten["route_mask"], ten["w_gate"],
+             ten["w_up"], ten["w_down"], ten.get("s_gate"), ten.get("s_up"), ten.get("s_down"))
+
+    def step(ev=None):
+        return run(*wargs, gate_up_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    gu_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    gu_avg = sum(gu_ms) / len(gu_ms)
+    log(f"whole path: {ms_step:.4f} ms/step (wall {1e3 * t_wall / args.steps:.4f}); "
+        f"gate/up stage avg {gu_avg:.4f} ms, median {gu_ms[len(gu_ms) // 2]:.4f} ms")
+
+    counts = run.rt.counts.cpu().numpy()[: wl.E].tolist()
+    work = algorithmic_work(wl, counts, wl.T)
+    tok_s = wl.T / (ms_step / 1e3)
+    # bound of the dominant stage: HBM time vs MFMA time at the published peaks
+    t_h = work["gate_up_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_m = work["gate_up_flops"] / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12)
+    if t_h >= t_m:
+        ach = work["gate_up_bytes"] / (gu_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = work["gate_up_flops"] / (gu_avg / 1e3) / 1e12
+        pk = MFMA_PEAK_TFLOPS[wl.dtype]
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": pk, "unit": "TFLOP/s",
+                "frac": round(ach / pk, 4)}
+    roof["traffic"] = traffic_from_profiles(name)
+    roof["kernel"] = "gate/up stage (skinny_kernel + fat_kernel, SwiGLU epilogue)"
+    roof["avg_ms"] = round(gu_avg, 5)
+    roof["algorithmic_bytes"] = int(work["gate_up_bytes"])
+    roof["algorithmic_flops"] = work["gate_up_flops"]
+    t_path_roof = max(work["path_bytes"] / (HBM_PEAK_GBS * 1e9),
+                      work["path_flops"] / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl, r, args.cpu_experts)
+        log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
+                   "routing": wl.routing, "mask_p": wl.mask_p, "weights": wl.dtype,
+                   "parallelism": "single-gpu"},
+        "path": {"tflops": round(work["path_flops"] / (ms_step / 1e3) / 1e12, 2),
+                 "algorithmic_gb": round(work["path_bytes"] / 1e9, 3),
+                 "hbm_gbs": round(work["path_bytes"] / (ms_step / 1e3) / 1e9, 1),
+                 "roofline_frac": round(t_path_roof / (ms_step / 1e3), 4),
+                 "active_rows": work["R_act"], "experts_used": work["experts_used"],
+                 "stage_bytes": work["stage_bytes"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_source_sha": source_hash(),
+    }
+    _ = np
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

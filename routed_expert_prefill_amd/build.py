@@ -1,0 +1,69 @@
+"""Build the gfx950 shared library ``libmoe_prefill.so`` in-tree with hipcc.
+
+Every HIP source is compiled for gfx950 only.  Packed-fp32 instructions are
+disabled at the target-feature level; no fast-math flag is used, so fp32
+division and square root stay correctly rounded (the fp8 quantiser relies on
+IEEE division).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmoe_prefill.so")
+
+HIP_SOURCES = ["route_build.hip", "combine.hip", "quant.hip", "ffn_bf16.hip", "ffn_fp8.hip"]
+HOST_SOURCES = ["api.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+          "-I" + os.path.join(ROOT, "include")]
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError("build failed: " + " ".join(cmd) + "\n" + out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append([cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        for out in ex.map(_run, jobs):
+            if verbose and out.strip():
+                print(out)
+    objs = [j[-1] for j in jobs]
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "--offload-arch=gfx950", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

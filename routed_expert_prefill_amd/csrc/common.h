@@ -1,0 +1,76 @@
+// Internal definitions shared by the gfx950 kernels of the routed-MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// One row-block of one expert: rows [row0, row0 + nrows) of the expert-sorted
+// route order all belong to expert e.
+struct Tile {
+  int e;
+  int row0;
+  int nrows;
+  int pad;
+};
+
+// Tile classes.  Skinny tiles hold up to 32 routed rows and stream their
+// expert's weights straight into MFMA operand registers; fat tiles hold up to
+// kFatRows rows and stage both operands through LDS.
+constexpr int kSkinnyMaxRows = 32;
+constexpr int kFatRows = 128;
+
+// Layout of the schedule at the start of the grouped-FFN workspace.
+struct Schedule {
+  int n_skinny;
+  int n_fat;
+  int pad[62];  // keeps the tile arrays 256-byte aligned
+};
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
+// supplies row (l % 16) of its operand and the 8 consecutive reduction
+// indices 8*(l/16) .. 8*(l/16)+7; lane l receives D[4*(l/16) + r][l % 16],
+// r = 0..3, where the first operand indexes D's rows.
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 E4M3 x E4M3 MFMA with unit block exponents (E8M0 127 = 2^0).
+// Each lane supplies 32 consecutive reduction indices 32*(l/16) .. +31 of
+// row (l % 16); the result layout is the bf16 one.
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// silu(g) * u in fp32.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const void *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace moe

@@ -1,0 +1,69 @@
+// Launch entry points of the gfx950 kernels, called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, int E,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                              int32_t *route_rows, int32_t *ws, hipStream_t stream);
+size_t route_build_ws_bytes(int R, int E);
+
+hipError_t launch_combine(const float *y, const int32_t *route_rows, const float *topk_w,
+                          const uint8_t *mask, int T, int k, int d, float *out,
+                          hipStream_t stream);
+
+int quant_max_cols();
+hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
+                             uint8_t *q, float *s, int grid_cap, hipStream_t stream);
+
+hipError_t launch_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *skinny, Tile *fat,
+                           hipStream_t stream);
+
+// Stages of the grouped FFN (bit mask).
+enum : int { kStagePlan = 1, kStageGateUp = 2, kStageDown = 4, kStageAll = 7 };
+
+// bf16 grouped FFN: schedule, gate/up + SwiGLU, down.
+struct FfnLaunch {
+  const uint16_t *x;
+  const int32_t *offsets;
+  const int32_t *sorted_routes;
+  const uint16_t *wg, *wu, *wd;
+  float *y;
+  uint16_t *h;
+  Schedule *sch;
+  Tile *skinny;
+  Tile *fat;
+  int T, k, E, d, f, R;
+  int grid_cap;  // persistent workgroups per GEMM launch
+};
+hipError_t launch_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
+
+// fp8 grouped FFN: plan (schedule + per-row quantisation of x into qx, sx),
+// gate/up + SwiGLU (h in bf16), down (per-row quantisation of h, then GEMM).
+struct FfnLaunchFp8 {
+  const uint16_t *x;
+  uint8_t *qx;
+  float *sx;
+  const int32_t *offsets;
+  const int32_t *sorted_routes;
+  const uint8_t *wg, *wu, *wd;
+  const float *sg, *su, *sd;
+  float *y;
+  uint16_t *h;
+  uint8_t *qh;
+  float *sh;
+  Schedule *sch;
+  Tile *skinny;
+  Tile *fat;
+  int T, k, E, d, f, R;
+  int grid_cap;
+};
+hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream);
+
+}  // namespace moe

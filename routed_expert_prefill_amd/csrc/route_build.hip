@@ -1,0 +1,158 @@
+// Route histogram, prefix and stable scatter for up to 256 experts
+// ("perf(ds4): batch heterogeneous MoE prefill by expert", Summary).
+//
+// Three launches over chunks of kChunk routes:
+//   1. per-chunk histogram in LDS (integer atomics: order-independent);
+//   2. one workgroup scans the chunk histograms per bin and the bin totals;
+//   3. per-chunk stable scatter: each wave walks its routes 64 at a time in
+//      route order, finds equal keys among the 64 lanes with one ballot per
+//      key bit, and ranks each lane among its earlier peers.
+// Results are integers and do not depend on scheduling.
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kRbThreads = 256;
+constexpr int kRbWaves = kRbThreads / kWave;
+constexpr int kChunk = 2048;  // routes per workgroup
+constexpr int kMaxBins = 257; // E + 1 with E <= 256
+
+__device__ __forceinline__ int route_key(const int32_t *ids, const uint8_t *mask, int r, int E) {
+  const int e = ids[r];
+  const bool act = (mask == nullptr || mask[r] != 0) && (unsigned)e < (unsigned)E;
+  return act ? e : E;
+}
+
+__global__ __launch_bounds__(kRbThreads) void rb_hist_kernel(const int32_t *__restrict__ ids,
+                                                             const uint8_t *__restrict__ mask,
+                                                             int R, int E,
+                                                             int32_t *__restrict__ chunk_hist) {
+  __shared__ int h[kMaxBins];
+  for (int b = threadIdx.x; b <= E; b += kRbThreads) h[b] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += kRbThreads) {
+    const int r = base + i;
+    if (r < R) atomicAdd(&h[route_key(ids, mask, r, E)], 1);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b <= E; b += kRbThreads) chunk_hist[(size_t)blockIdx.x * (E + 1) + b] = h[b];
+}
+
+// One workgroup of 512 threads: bin b's chunk prefix, bin totals, offsets.
+constexpr int kScanThreads = 512;
+
+__global__ __launch_bounds__(kScanThreads) void rb_scan_kernel(const int32_t *__restrict__ chunk_hist,
+                                                               int nchunks, int E,
+                                                               int32_t *__restrict__ counts,
+                                                               int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ chunk_base) {
+  __shared__ int tot[kScanThreads];
+  const int b = threadIdx.x;
+  int s = 0;
+  if (b <= E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const size_t idx = (size_t)c * (E + 1) + b;
+      const int v = chunk_hist[idx];
+      chunk_base[idx] = s;
+      s += v;
+    }
+    counts[b] = s;
+  }
+  tot[b] = (b <= E) ? s : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the bins
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = (b >= off) ? tot[b - off] : 0;
+    __syncthreads();
+    tot[b] += v;
+    __syncthreads();
+  }
+  const int excl = (b == 0) ? 0 : tot[b - 1];
+  if (b <= E + 1) offsets[b] = excl;
+  if (b <= E) {
+    for (int c = 0; c < nchunks; ++c) chunk_base[(size_t)c * (E + 1) + b] += excl;
+  }
+}
+
+__global__ __launch_bounds__(kRbThreads) void rb_scatter_kernel(const int32_t *__restrict__ ids,
+                                                                const uint8_t *__restrict__ mask,
+                                                                int R, int E, int key_bits,
+                                                                const int32_t *__restrict__ chunk_base,
+                                                                int32_t *__restrict__ sorted_routes,
+                                                                int32_t *__restrict__ route_rows) {
+  __shared__ int cnt[kRbWaves][kMaxBins];
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  for (int i = threadIdx.x; i < kRbWaves * kMaxBins; i += kRbThreads) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  constexpr int kPerWave = kChunk / kRbWaves;
+  const int wbase = blockIdx.x * kChunk + w * kPerWave;
+
+  // pass 1: per-wave key counts
+  for (int g = 0; g < kPerWave; g += kWave) {
+    const int r = wbase + g + lane;
+    if (r < R) atomicAdd(&cnt[w][route_key(ids, mask, r, E)], 1);
+  }
+  __syncthreads();
+  // per bin: the chunk's base plus the counts of the earlier waves
+  for (int b = threadIdx.x; b <= E; b += kRbThreads) {
+    int s = chunk_base[(size_t)blockIdx.x * (E + 1) + b];
+    for (int v = 0; v < kRbWaves; ++v) {
+      const int c = cnt[v][b];
+      cnt[v][b] = s;
+      s += c;
+    }
+  }
+  __syncthreads();
+
+  // pass 2: ordered placement, 64 routes at a time
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < kPerWave; g += kWave) {
+    const int r = wbase + g + lane;
+    const bool valid = r < R;
+    const int key = valid ? route_key(ids, mask, r, E) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < key_bits; ++bit) {
+      const bool set = (key >> bit) & 1;
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    int pos = 0;
+    if (valid) pos = cnt[w][key] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) cnt[w][key] = pos + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted_routes[pos] = r;
+      route_rows[r] = pos;
+    }
+  }
+}
+
+int route_chunks(int R) { return (R + kChunk - 1) / kChunk; }
+
+hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, int E,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                              int32_t *route_rows, int32_t *ws, hipStream_t stream) {
+  const int nchunks = route_chunks(R);
+  int32_t *chunk_hist = ws;
+  int32_t *chunk_base = ws + (size_t)nchunks * (E + 1);
+  int key_bits = 1;
+  while ((1 << key_bits) < E + 1) ++key_bits;
+  hipLaunchKernelGGL(rb_hist_kernel, dim3(nchunks), dim3(kRbThreads), 0, stream, ids, mask, R, E,
+                     chunk_hist);
+  hipLaunchKernelGGL(rb_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nchunks,
+                     E, counts, offsets, chunk_base);
+  hipLaunchKernelGGL(rb_scatter_kernel, dim3(nchunks), dim3(kRbThreads), 0, stream, ids, mask, R,
+                     E, key_bits, chunk_base, sorted_routes, route_rows);
+  return hipGetLastError();
+}
+
+size_t route_build_ws_bytes(int R, int E) {
+  return (size_t)2 * route_chunks(R) * (E + 1) * sizeof(int32_t);
+}
+
+}  // namespace moe

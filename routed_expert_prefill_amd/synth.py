@@ -223,3 +223,44 @@ __all__ = [
     "expert_weights", "all_expert_weights", "SCALE_BLOCK", "weight_bytes_per_expert",
     "approx_host_bytes", "f32_to_bf16_bits", "f32_to_e4m3_codes",
 ]
+
+
+def device_inputs(wl: Workload, seed: int = 0, device="cuda", threads: Optional[int] = None):
+    """Generate a workload straight into device tensors (host memory stays O(one expert)).
+
+    Returns (routing [numpy], tensors dict): x bf16 [T,d], topk_ids int32, topk_w fp32,
+    route_mask uint8, w_gate/w_up [E,f,d] and w_down [E,d,f] (bf16, or uint8 E4M3 codes
+    with s_gate/s_up/s_down fp32 block scales for fp8 workloads).
+    """
+    import torch
+
+    dev = torch.device(device)
+    r = make_routing(wl, seed)
+    T, E, d, f = wl.T, wl.E, wl.d, wl.f
+    fp8 = wl.dtype == "fp8"
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    ten = {
+        "x": torch.from_numpy(r.x.view(np.int16)).view(torch.bfloat16).to(dev),
+        "topk_ids": torch.from_numpy(r.topk_ids).to(dev),
+        "topk_w": torch.from_numpy(r.topk_w).to(dev),
+        "route_mask": torch.from_numpy(r.route_mask).to(dev),
+        "w_gate": torch.empty((E, f, d), dtype=wdt, device=dev),
+        "w_up": torch.empty((E, f, d), dtype=wdt, device=dev),
+        "w_down": torch.empty((E, d, f), dtype=wdt, device=dev),
+    }
+    if fp8:
+        ten["s_gate"] = torch.empty((E, f // SCALE_BLOCK, d // SCALE_BLOCK), dtype=torch.float32, device=dev)
+        ten["s_up"] = torch.empty((E, f // SCALE_BLOCK, d // SCALE_BLOCK), dtype=torch.float32, device=dev)
+        ten["s_down"] = torch.empty((E, d // SCALE_BLOCK, f // SCALE_BLOCK), dtype=torch.float32, device=dev)
+    names = {"wg": "w_gate", "wu": "w_up", "wd": "w_down", "sg": "s_gate", "su": "s_up", "sd": "s_down"}
+
+    def sink(e, w):
+        for k, a in w.items():
+            src = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+            if a.dtype == np.uint16:
+                src = src.view(torch.bfloat16)
+            ten[names[k]][e].copy_(src)
+
+    all_expert_weights(wl, seed, threads=threads, sink=sink)
+    torch.cuda.synchronize(dev)
+    return r, ten

@@ -1,0 +1,73 @@
+"""GPU combine vs the fp64 oracle combine (1e-6 relative, the differential
+tolerance the fused-combine qualification used), exact zeros for masked
+routes, +0.0 for tokens with no active route, power-of-two exactness."""
+import numpy as np
+import pytest
+
+from oracle.moe import combine_ref
+from gpu_util import np_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(y, rr, w, mask):
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    out = rep.combine(np_dev(y), np_dev(rr), np_dev(w), None if mask is None else np_dev(mask))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _case(seed, T, k, d, p):
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((T * k, d)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    mask = (rng.random((T, k)) >= p).astype(np.uint8)
+    rr = rng.permutation(T * k).astype(np.int32)
+    return y, rr, w, mask
+
+
+@pytest.mark.parametrize("seed,T,k,d,p", [(0, 401, 6, 4096, 0.05), (1, 3, 1, 4, 0.0),
+                                          (2, 33, 16, 1028, 0.5), (3, 1, 6, 8, 1.0)])
+def test_matches_oracle(seed, T, k, d, p):
+    y, rr, w, mask = _case(seed, T, k, d, p)
+    got = _run(y, rr, w, mask)
+    ref = combine_ref(y, rr, w, mask, T, k)
+    scale = np.abs(y).max() * np.abs(w).sum(axis=1).max()
+    assert np.abs(got - ref).max() <= 1e-6 * scale
+
+
+def test_masked_routes_never_read():
+    T, k, d = 64, 6, 256
+    y, rr, w, mask = _case(5, T, k, d, 0.3)
+    mask[0] = 0
+    base = _run(y, rr, w, mask)
+    yp, wp = y.copy(), w.copy()
+    rrp = rr.copy().reshape(T, k)
+    for t in range(T):
+        for j in range(k):
+            if not mask[t, j]:
+                yp[rr[t * k + j]] = np.nan
+                wp[t, j] = np.inf
+                rrp[t, j] = 2 ** 30  # far out of range: must not be dereferenced
+    got = _run(yp, rrp.reshape(-1), wp, mask)
+    assert np.array_equal(base.view(np.uint32), got.view(np.uint32))
+    assert np.all(base[0].view(np.uint32) == 0)  # +0.0 bits
+
+
+def test_signed_zero_and_scaling():
+    T, k, d = 16, 4, 64
+    y, rr, w, mask = _case(6, T, k, d, 0.2)
+    y[rr[0:k]] = -0.0  # token 0 sums only negative zeros -> +0.0
+    a = _run(y, rr, w, mask)
+    assert np.all(a[0].view(np.uint32) == 0)
+    b = _run(y, rr, (w * 8).astype(np.float32), mask)
+    assert np.array_equal((a * 8).view(np.uint32), b.view(np.uint32))
+
+
+def test_no_mask_means_all_active():
+    y, rr, w, _ = _case(7, 10, 3, 32, 0.0)
+    ones = np.ones((10, 3), np.uint8)
+    assert np.array_equal(_run(y, rr, w, None), _run(y, rr, w, ones))

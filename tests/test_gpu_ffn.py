@@ -1,0 +1,171 @@
+"""GPU grouped FFN + combine vs the fp64 per-token oracle.
+
+Tolerances: bf16 max-abs <= 2e-2 and relative Frobenius <= 1e-3; fp8
+5e-2 / 5e-3.  Both sides round h to bf16 (and quantise x and h per row in
+fp8) at the same point, so what is left is fp32 accumulation order and rare
+bf16 rounding-boundary flips of h.
+
+The per-expert row counts below put experts in every tile class: 1-16 rows
+(one 16-row skinny slab), 17-32 (two slabs), 33-128 (one fat tile), >128
+(full fat tiles plus a skinny or fat remainder), and empty experts.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe as omoe
+from oracle.route import route_table
+from gpu_util import bf16_dev, np_dev, rel_frob, routing_with_counts
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = (2e-2, 1e-3)
+FP8_TOL = (5e-2, 5e-3)
+
+
+def _weights(E, d, f, fp8, seed, w_std=0.02):
+    import torch
+
+    rng = np.random.default_rng(seed)
+    W = {}
+    shapes = {"wg": (E, f, d), "wu": (E, f, d), "wd": (E, d, f)}
+    for n, shp in shapes.items():
+        z = rng.standard_normal(shp).astype(np.float32)
+        if fp8:
+            z = np.clip(z * 112.0, -448, 448).astype(np.float32)
+            W[n] = torch.from_numpy(z).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        else:
+            W[n] = torch.from_numpy(z * np.float32(w_std)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if fp8:
+        for n, src in (("sg", "wg"), ("su", "wu"), ("sd", "wd")):
+            e, r, c = shapes[src]
+            W[n] = (rng.uniform(0.5, 2.0, (e, r // 128, c // 128)) * (w_std / 448.0)).astype(np.float32)
+    return W
+
+
+def _x(T, d, seed, std=1.0):
+    import torch
+
+    rng = np.random.default_rng(seed + 1000)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32) * np.float32(std))
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _dev_weights(W, fp8):
+    if fp8:
+        return {n: np_dev(a) for n, a in W.items()}
+    return {n: bf16_dev(a) for n, a in W.items()}
+
+
+def _run(ids, w, mask, x, W, E, fp8, y_fill=None):
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    T, k = ids.shape
+    d = x.shape[1]
+    f = W["wg"].shape[1]
+    Wd = _dev_weights(W, fp8)
+    run = rep.MoEPrefill(T, k, E, d, f, fp8=fp8)
+    if y_fill is not None:
+        run.y.fill_(y_fill)
+    out = run(bf16_dev(x), np_dev(ids), np_dev(w), np_dev(mask), Wd["wg"], Wd["wu"], Wd["wd"],
+              Wd.get("sg"), Wd.get("su"), Wd.get("sd"))
+    torch.cuda.synchronize()
+    return run, out.cpu().numpy().astype(np.float64)
+
+
+def _check(got, ref, tol):
+    err = np.abs(got - ref).max()
+    rel = rel_frob(got, ref)
+    assert err <= tol[0] and rel <= tol[1], (err, rel)
+    return err, rel
+
+
+CLASS_COUNTS = [0, 1, 7, 16, 17, 31, 32, 33, 64, 128, 129, 160, 161, 300, 0, 2]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_tile_classes(fp8):
+    E = len(CLASS_COUNTS)
+    d, f = (256, 256) if fp8 else (384, 256)
+    ids, mask = routing_with_counts(CLASS_COUNTS, 6, seed=1, masked_extra=13)
+    T, k = ids.shape
+    rng = np.random.default_rng(2)
+    w = rng.random((T, k)).astype(np.float32)
+    x = _x(T, d, 3)
+    W = _weights(E, d, f, fp8, 4)
+    run, out = _run(ids, w, mask, x, W, E, fp8, y_fill=float("nan"))
+    # routes reach y in sorted order; masked rows (>= offsets[E]) are never written
+    rt = route_table(ids, mask, E)
+    assert np.array_equal(run.rt.offsets.cpu().numpy(), rt.offsets)
+    y = run.y.cpu().numpy()
+    n_act = int(rt.offsets[E])
+    assert np.all(np.isnan(y[n_act:]))
+    assert not np.any(np.isnan(y[:n_act]))
+    src = omoe.dict_source(W)
+    # per-route FFN outputs on a sample of routes from every expert
+    sample = [int(rt.sorted_routes[i]) for i in range(0, n_act, 7)]
+    yr = omoe.route_outputs_ref(x, ids, src, sample, fp8=fp8)
+    _check(y[rt.route_rows[sample]], yr, FP8_TOL if fp8 else BF16_TOL)
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, src, E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_tiny_workload_random_routing(fp8):
+    rng = np.random.default_rng(5)
+    T, k, E, d, f = 45, 6, 16, 512, 256
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    mask = (rng.random((T, k)) >= 0.1).astype(np.uint8)
+    mask[3] = 0  # a token with no active route
+    w = rng.random((T, k)).astype(np.float32)
+    x = _x(T, d, 6)
+    W = _weights(E, d, f, fp8, 7)
+    _, out = _run(ids, w, mask, x, W, E, fp8)
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+    assert np.all(out[3] == 0) and not np.any(np.signbit(out[3]))
+
+
+def test_single_expert_single_route_is_dense_mlp():
+    """E = 1, k = 1, gate 1, no mask: a dense SwiGLU MLP, checked also against
+    torch's own matmul on the GPU (an independent library product)."""
+    import torch
+
+    T, d, f = 300, 512, 384
+    ids = np.zeros((T, 1), np.int32)
+    mask = np.ones((T, 1), np.uint8)
+    w = np.ones((T, 1), np.float32)
+    x = _x(T, d, 8)
+    W = _weights(1, d, f, False, 9)
+    _, out = _run(ids, w, mask, x, W, 1, False)
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), 1)
+    _check(out, ref, BF16_TOL)
+    X = bf16_dev(x).float()
+    Wg, Wu, Wd = (bf16_dev(W[n][0]).float() for n in ("wg", "wu", "wd"))
+    h = (torch.nn.functional.silu(X @ Wg.T) * (X @ Wu.T)).to(torch.bfloat16).float()
+    lib_ref = (h @ Wd.T).cpu().numpy()
+    _check(out, lib_ref, BF16_TOL)
+
+
+def test_deterministic_and_zero_input():
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    ids, mask = routing_with_counts([40, 3, 0, 150, 20], 4, seed=10, masked_extra=5)
+    T, k = ids.shape
+    E, d, f = 5, 256, 256
+    w = np.random.default_rng(1).random((T, k)).astype(np.float32)
+    x = _x(T, d, 11)
+    W = {n: bf16_dev(a) for n, a in _weights(E, d, f, False, 12).items()}
+    run = rep.MoEPrefill(T, k, E, d, f)
+    args = (np_dev(ids), np_dev(w), np_dev(mask), W["wg"], W["wu"], W["wd"])
+    first = run(bf16_dev(x), *args).clone()
+    for _ in range(4):
+        run.ffn_ws.fill_(0xFF)  # stale workspace contents must not matter
+        again = run(bf16_dev(x), *args)
+        assert torch.equal(first.view(torch.int32), again.view(torch.int32))
+    zero = run(bf16_dev(np.zeros_like(x)), *args)
+    torch.cuda.synchronize()
+    assert torch.all(zero.view(torch.int32) == 0)

@@ -1,0 +1,46 @@
+"""GPU per-row E4M3 quantisation vs the oracle: codes and scales bit-exact."""
+import numpy as np
+import pytest
+
+from oracle import numerics as nx
+from routed_expert_prefill_amd.synth import f32_to_bf16_bits
+from gpu_util import bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(xbits):
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    q, s = rep.quant_rows_fp8(bf16_dev(xbits))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,scale", [(64, 4096, 1.0), (37, 2048, 3e-3), (5, 128, 50.0),
+                                             (300, 16384, 1.0), (8, 256, 2.0 ** -60)])
+def test_matches_oracle(rows, cols, scale):
+    rng = np.random.default_rng(rows + cols)
+    x = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
+    x[0, :5] = [0.0, -0.0, 1e-30, -1e-30, 0.0]
+    bits = f32_to_bf16_bits(x)
+    q, s = _gpu(bits)
+    qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+
+
+def test_zero_rows_and_wide_dynamic_range():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 512)).astype(np.float32)
+    x[1] = 0.0
+    x[2] = -0.0
+    x[3, 7] = 3e4  # one large value pushes the rest into the subnormal codes
+    x[4] *= 1e-6
+    bits = f32_to_bf16_bits(x)
+    q, s = _gpu(bits)
+    qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
+    assert np.array_equal(q, qr) and np.array_equal(s, sr)
+    assert s[1] == 1.0 and not q[1].any() and not q[2].any()
