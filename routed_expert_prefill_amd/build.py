@@ -42,26 +42,30 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile all sources and link the shared library; returns its path.
+
+    defines: extra -D flags (tuning knobs; the defaults are the shipped values).
+    """
+    os.makedirs(build_dir, exist_ok=True)
+    extra = ["-D" + d for d in defines]
     cc = hipcc()
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        jobs.append([cc, *COMMON, *extra, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append([cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        jobs.append([cc, *COMMON, *extra, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        for out in ex.map(_run, jobs):
-            if verbose and out.strip():
-                print(out)
+        for log in ex.map(_run, jobs):
+            if verbose and log.strip():
+                print(log)
     objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, "-shared", "--offload-arch=gfx950", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

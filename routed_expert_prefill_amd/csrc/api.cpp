@@ -5,7 +5,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/moe_prefill.h"
+#include "moe_prefill.h"
 #include "kernels.h"
 
 
@@ -19,19 +19,27 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 int status_from(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// Persistent workgroups per GEMM launch: a few per compute unit.
-int grid_cap_for_current_device() {
+int num_cus_current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
-    return 1024;
-  return cus * 4;
+    return 256;
+  return cus;
+}
+
+// Persistent workgroups per GEMM launch: a few per compute unit.
+int grid_cap_for_current_device() {
+  const int cus = num_cus_current_device();
+#ifndef MOE_GRID_PER_CU
+#define MOE_GRID_PER_CU 4
+#endif
+  return cus * MOE_GRID_PER_CU;
 }
 
 struct FfnLayout {
-  size_t sched, skinny, fat, h, qx, sx, qh, sh, total;
+  size_t sched, skinny, fat, big, h, qx, sx, qh, sh, total;
 };
 
 bool ffn_desc_status(const moe_ffn_desc *d, int *st) {
@@ -79,6 +87,8 @@ FfnLayout ffn_layout(const moe_ffn_desc *d) {
   off += align_up(sizeof(moe::Tile) * (size_t)d->E);
   L.fat = off;
   off += align_up(sizeof(moe::Tile) * (R / moe::kFatRows + (size_t)d->E));
+  L.big = off;
+  off += align_up(sizeof(moe::Tile) * (R / moe::kBigRows + (size_t)d->E));
   L.h = off;
   off += align_up(R * (size_t)d->f * 2);
   if (fp8) {
@@ -186,6 +196,8 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
     L.sch = reinterpret_cast<moe::Schedule *>(ws + lay.sched);
     L.skinny = reinterpret_cast<moe::Tile *>(ws + lay.skinny);
     L.fat = reinterpret_cast<moe::Tile *>(ws + lay.fat);
+    L.big = reinterpret_cast<moe::Tile *>(ws + lay.big);
+    L.num_cus = num_cus_current_device();
     L.T = desc->T;
     L.k = desc->k;
     L.E = desc->E;
@@ -214,6 +226,8 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
   L.sch = reinterpret_cast<moe::Schedule *>(ws + lay.sched);
   L.skinny = reinterpret_cast<moe::Tile *>(ws + lay.skinny);
   L.fat = reinterpret_cast<moe::Tile *>(ws + lay.fat);
+  L.big = reinterpret_cast<moe::Tile *>(ws + lay.big);
+  L.num_cus = num_cus_current_device();
   L.T = desc->T;
   L.k = desc->k;
   L.E = desc->E;

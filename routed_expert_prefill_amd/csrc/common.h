@@ -8,6 +8,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -22,17 +23,23 @@ struct Tile {
   int pad;
 };
 
-// Tile classes.  Skinny tiles hold up to 32 routed rows and stream their
-// expert's weights straight into MFMA operand registers; fat tiles hold up to
-// kFatRows rows and stage both operands through LDS.
+// Tile classes.  An expert's segment of n rows is cut into full big tiles of
+// kBigRows rows; the remainder r becomes one big tile if r > kFatRows, one fat
+// tile if kSkinnyMaxRows < r <= kFatRows, and one skinny tile otherwise.
+//  skinny: <= 32 rows, weights streamed straight into MFMA operand registers;
+//  fat:    <= 128 rows, both operands staged through LDS by the waves;
+//  big:    <= 256 rows, both operands streamed into an LDS ring by direct
+//          global->LDS loads.
 constexpr int kSkinnyMaxRows = 32;
 constexpr int kFatRows = 128;
+constexpr int kBigRows = 256;
 
 // Layout of the schedule at the start of the grouped-FFN workspace.
 struct Schedule {
   int n_skinny;
   int n_fat;
-  int pad[62];  // keeps the tile arrays 256-byte aligned
+  int n_big;
+  int pad[61];  // keeps the tile arrays 256-byte aligned
 };
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
@@ -41,6 +48,14 @@ struct Schedule {
 // r = 0..3, where the first operand indexes D's rows.
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies row (l % 32) of its
+// operand and reduction indices 8*(l/32) .. 8*(l/32)+7; register j of lane l
+// receives D[8*(j/4) + 4*(l/32) + j%4][l % 32].  On gfx950 this shape runs at
+// the full bf16 rate; the 16x16x32 shape issues at half of it.
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // 16x16x128 E4M3 x E4M3 MFMA with unit block exponents (E8M0 127 = 2^0).

@@ -301,13 +301,13 @@ static int cap_grid8(long long items, int cap) {
 hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream) {
   hipError_t err = hipSuccess;
   if (stages & kStagePlan) {
-    err = launch_schedule(L.offsets, L.E, L.sch, L.skinny, L.fat, stream);
+    err = launch_schedule(L.offsets, L.E, L.sch, L.skinny, L.fat, nullptr, stream);
     if (err != hipSuccess) return err;
     err = launch_quant_rows(L.x, L.T, nullptr, L.d, L.qx, L.sx, L.grid_cap, stream);
     if (err != hipSuccess) return err;
   }
   const long long max_skinny = L.E < L.R ? L.E : L.R;
-  const long long max_fat = L.R / kFatRows + L.E;
+  const long long max_fat = L.R / kFatRows + L.E;  // no big class: fat tiles only
 
   GemmArgs8 gu{};
   gu.act = L.qx;

@@ -23,7 +23,7 @@ hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_de
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream);
 
 hipError_t launch_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *skinny, Tile *fat,
-                           hipStream_t stream);
+                           Tile *big, hipStream_t stream);
 
 // Stages of the grouped FFN (bit mask).
 enum : int { kStagePlan = 1, kStageGateUp = 2, kStageDown = 4, kStageAll = 7 };
@@ -39,8 +39,10 @@ struct FfnLaunch {
   Schedule *sch;
   Tile *skinny;
   Tile *fat;
+  Tile *big;
   int T, k, E, d, f, R;
   int grid_cap;  // persistent workgroups per GEMM launch
+  int num_cus;
 };
 hipError_t launch_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
 
@@ -61,8 +63,10 @@ struct FfnLaunchFp8 {
   Schedule *sch;
   Tile *skinny;
   Tile *fat;
+  Tile *big;
   int T, k, E, d, f, R;
   int grid_cap;
+  int num_cus;
 };
 hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream);
 
