@@ -26,8 +26,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 METRIC = "routed-MoE prefill tokens/s + % of MFMA/HBM roofline at T=401/2048/8192"
-KERNEL_SOURCES = ["routed_expert_prefill_amd/csrc/ffn_bf16.hip",
+KERNEL_SOURCES = ["routed_expert_prefill_amd/csrc/ffn_grouped.hip",
                   "routed_expert_prefill_amd/csrc/ffn_fp8.hip",
+                  "routed_expert_prefill_amd/csrc/ring.h",
                   "routed_expert_prefill_amd/csrc/common.h"]
 
 
@@ -209,7 +210,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(ach / pk, 4)}
     roof["traffic"] = traffic_from_profiles(name)
-    roof["kernel"] = "gate/up stage (skinny_kernel + fat_kernel, SwiGLU epilogue)"
+    roof["kernel"] = ("grouped_gemm_kernel<true> (gate/up GEMM, SwiGLU epilogue)" if not fp8 else
+                      "gate/up stage (skinny8_kernel + fat8_kernel, SwiGLU epilogue)")
     roof["avg_ms"] = round(gu_avg, 5)
     roof["algorithmic_bytes"] = int(work["gate_up_bytes"])
     roof["algorithmic_flops"] = work["gate_up_flops"]

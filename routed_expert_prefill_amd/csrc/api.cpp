@@ -205,7 +205,7 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
     L.f = desc->f;
     L.R = R;
     L.grid_cap = cap;
-    return status_from(moe::launch_ffn_bf16(L, stages, s));
+    return status_from(moe::launch_grouped_ffn_bf16(L, stages, s));
   }
   moe::FfnLaunchFp8 L{};
   L.x = static_cast<const uint16_t *>(x);

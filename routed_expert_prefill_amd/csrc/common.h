@@ -39,7 +39,9 @@ struct Schedule {
   int n_skinny;
   int n_fat;
   int n_big;
-  int pad[61];  // keeps the tile arrays 256-byte aligned
+  int n_tiles;     // all tiles of the single ordered list (bf16 path)
+  int counter[2];  // work-queue heads of the gate/up and down kernels
+  int pad[58];     // keeps the tile arrays 256-byte aligned
 };
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l

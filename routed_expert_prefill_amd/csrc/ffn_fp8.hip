@@ -57,6 +57,100 @@ __device__ __forceinline__ void store_out8(const GemmArgs8 &a, int row, int n, f
   }
 }
 
+// ------------------------------------------------------------------ schedule
+//
+// Tiles of the fp8 path: each expert's segment is cut into 128-row fat tiles
+// and a remainder (a fat tile if it holds more than 32 rows, else a skinny
+// tile), written to two lists.
+
+constexpr int kSchedThreads = 256;
+
+__device__ int block_excl_scan(int v, int *total, int *buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int a = (t >= off) ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += a;
+    __syncthreads();
+  }
+  const int incl = buf[t];
+  *total = buf[kSchedThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *__restrict__ offsets,
+                                                                 int E, Schedule *sch,
+                                                                 Tile *__restrict__ skinny,
+                                                                 Tile *__restrict__ fat,
+                                                                 Tile *__restrict__ big) {
+  __shared__ int buf[kSchedThreads];
+  const int e = threadIdx.x;
+  int n = 0, row0 = 0;
+  if (e < E) {
+    row0 = offsets[e];
+    n = offsets[e + 1] - row0;
+  }
+  // full big tiles, then one tile for the remainder chosen by its size
+  int nb = 0, rem = n;
+  if (big != nullptr) {
+    nb = n / kBigRows;
+    rem = n - nb * kBigRows;
+    if (rem > kFatRows) {
+      ++nb;
+      rem = 0;
+    }
+  }
+  int nf = 0;
+  if (big == nullptr) {  // no big class: cut into fat tiles
+    nf = rem / kFatRows;
+    rem -= nf * kFatRows;
+  }
+  if (rem > kSkinnyMaxRows) {
+    ++nf;
+    rem = -rem;  // marks "remainder is one fat tile"
+  }
+  const int cs = rem > 0 ? 1 : 0;
+  int tot_s, tot_f, tot_b;
+  const int ps = block_excl_scan(cs, &tot_s, buf);
+  const int pf = block_excl_scan(nf, &tot_f, buf);
+  const int pb = block_excl_scan(nb, &tot_b, buf);
+  int r = row0;
+  for (int i = 0; i < nb; ++i) {
+    Tile t;
+    t.e = e;
+    t.row0 = r;
+    t.nrows = min(kBigRows, row0 + n - r);
+    t.pad = 0;
+    big[pb + i] = t;
+    r += t.nrows;
+  }
+  for (int i = 0; i < nf; ++i) {
+    Tile t;
+    t.e = e;
+    t.row0 = r;
+    t.nrows = min(kFatRows, row0 + n - r);
+    t.pad = 0;
+    fat[pf + i] = t;
+    r += t.nrows;
+  }
+  if (cs) {
+    Tile t;
+    t.e = e;
+    t.row0 = r;
+    t.nrows = rem;
+    t.pad = 0;
+    skinny[ps] = t;
+  }
+  if (e == 0) {
+    sch->n_skinny = tot_s;
+    sch->n_fat = tot_f;
+    sch->n_big = tot_b;
+  }
+}
+
 // ------------------------------------------------------------------ skinny tiles
 
 constexpr int kSk8Threads = 256;
@@ -292,6 +386,14 @@ __global__ __launch_bounds__(kFt8Threads) void fat8_kernel(GemmArgs8 a) {
 }
 
 // ------------------------------------------------------------------ host side
+
+hipError_t launch_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *skinny, Tile *fat,
+                           Tile *big, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, offsets, E, sch,
+                     skinny, fat, big);
+  return hipGetLastError();
+}
+
 
 static int cap_grid8(long long items, int cap) {
   if (items < 1) items = 1;

@@ -1,0 +1,349 @@
+// Persistent grouped GEMM for the bf16 routed-MoE FFN: one kernel per
+// projection (gate/up with the SwiGLU epilogue, then down) that pulls work
+// items from a device queue.
+//
+// The expert-major grouping of "perf(ds4): batch heterogeneous MoE prefill by
+// expert" (Summary): every expert's routed rows form one contiguous segment
+// of the sorted route order and are multiplied by its weights together.  The
+// schedule cuts each segment into row tiles whose height adapts to the rows
+// the expert received (adaptive MoE tiles and a persistent compact work
+// queue, "perf(ds4): unify gfx1151 sparse-prefill stack", Composition):
+// 256-row tiles, then one remainder tile of 32, 64, 128 or 256 rows.  The
+// tile list is ordered tallest class first and each workgroup repeatedly
+// takes the next item (tile, 128 or 256 output features) from an atomic
+// counter, so memory-bound items of small experts run on some compute units
+// while compute-bound items of large experts run on others.
+//
+// Every item streams both operands through the LDS stage ring (ring.h): 256
+// weight rows and 32 x ablk activation rows per 32-element reduction stage,
+// kGgStages - 1 stages in flight while one is consumed.  MFMAs are 32x32x16
+// bf16; eight waves (two per SIMD, so one wave's matrix work covers the
+// other's barrier and LDS waits) each own 32-row weight tiles:
+//   ablk = 8 (256 rows): wave w takes weight tiles 2(w%4), 2(w%4)+1 and the
+//                        four activation tiles of half w/4;
+//   ablk < 8:            wave w takes weight tile w and every activation tile.
+// Gate/up weight rows are interleaved in 16-row groups (16 gate features,
+// the same 16 up features, ...), so one 32x32 tile holds both halves of the
+// SwiGLU for 16 features: registers 0-7 gate, 8-15 up.
+#include "kernels.h"
+#include "ring.h"
+
+namespace moe {
+
+struct GgArgs {
+  const uint16_t *act;           // gate/up: x [T, K]; down: h [R, K]
+  const int32_t *sorted_routes;  // gate/up: token of sorted row i is sorted_routes[i] / k
+  int k;
+  const uint16_t *w0;  // gate (or down) weights [E, N, K]
+  const uint16_t *w1;  // up weights [E, N, K] (gate/up only)
+  void *out;           // gate/up: h bf16 [R, N]; down: y fp32 [R, N]
+  int N, K;
+  const Tile *tiles;   // tile.pad = ablk (row capacity / 32)
+  const int *ntiles;
+  int *counter;        // item queue head, zeroed by the schedule
+};
+
+constexpr int kGgThreads = 512;
+constexpr int kGgWaves = kGgThreads / kWave;
+#ifndef MOE_GG_STAGES
+#define MOE_GG_STAGES 4
+#endif
+constexpr int kGgStages = MOE_GG_STAGES;  // ring slots: kGgStages - 1 stages in flight
+constexpr int kGgWRows = 256;
+constexpr int kGgSlot = (kBigRows + kGgWRows) * 64;  // bytes per ring slot (32 KB)
+
+// ------------------------------------------------------------------ schedule
+
+constexpr int kGsThreads = 256;
+
+__device__ int gs_scan(int v, int *total, int *buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kGsThreads; off <<= 1) {
+    const int x = (t >= off) ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += x;
+    __syncthreads();
+  }
+  const int incl = buf[t];
+  *total = buf[kGsThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// One thread per expert: full 256-row tiles, then one remainder tile whose
+// height is the smallest of 32, 64, 128, 256 that holds it.  Tiles are
+// written tallest class first.
+__global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
+    const int32_t *__restrict__ offsets, int E, Schedule *sch, Tile *__restrict__ tiles) {
+  __shared__ int buf[kGsThreads];
+  const int e = threadIdx.x;
+  int n = 0, row0 = 0;
+  if (e < E) {
+    row0 = offsets[e];
+    n = offsets[e + 1] - row0;
+  }
+  const int nfull = n / kBigRows;
+  const int rem = n - nfull * kBigRows;
+  const int rab = rem == 0 ? 0 : rem <= 32 ? 1 : rem <= 64 ? 2 : rem <= 128 ? 4 : 8;
+  int cnt[4] = {nfull + (rab == 8), rab == 4, rab == 2, rab == 1};  // ablk 8, 4, 2, 1
+  int pos[4], tot[4];
+  for (int c = 0; c < 4; ++c) pos[c] = gs_scan(cnt[c], &tot[c], buf);
+  int base = 0;
+  for (int c = 0; c < 4; ++c) {
+    pos[c] += base;
+    base += tot[c];
+  }
+  for (int i = 0; i < cnt[0]; ++i) {
+    Tile t;
+    t.e = e;
+    t.row0 = row0 + i * kBigRows;
+    t.nrows = min(kBigRows, n - i * kBigRows);
+    t.pad = 8;
+    tiles[pos[0] + i] = t;
+  }
+  if (rab > 0 && rab < 8) {
+    const int c = rab == 4 ? 1 : rab == 2 ? 2 : 3;
+    Tile t;
+    t.e = e;
+    t.row0 = row0 + nfull * kBigRows;
+    t.nrows = rem;
+    t.pad = rab;
+    tiles[pos[c]] = t;
+  }
+  if (e == 0) {
+    sch->n_big = tot[0];
+    sch->n_fat = tot[1] + tot[2];
+    sch->n_skinny = tot[3];
+    sch->n_tiles = base;
+    sch->counter[0] = 0;
+    sch->counter[1] = 0;
+  }
+}
+
+// ------------------------------------------------------------------ one item
+
+template <bool GATEUP>
+__device__ __forceinline__ void gg_store(const GgArgs &a, int row, int n, const f32x4 &g,
+                                         const f32x4 &u) {
+  if constexpr (GATEUP) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16_bits(swiglu(g[0], u[0])) |
+          ((uint32_t)f32_to_bf16_bits(swiglu(g[1], u[1])) << 16);
+    v.y = (uint32_t)f32_to_bf16_bits(swiglu(g[2], u[2])) |
+          ((uint32_t)f32_to_bf16_bits(swiglu(g[3], u[3])) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)row * a.N + n) = v;
+  } else {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (size_t)row * a.N + n) = g;
+  }
+}
+
+__device__ __forceinline__ f32x4 quad(const f32x16 &v, int g) {
+  return f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+}
+
+// Operand tiles a wave multiplies for one stage: TT activation tiles and TW
+// weight tiles of 32 rows, for the two 16-wide reduction steps.
+template <int AB>
+struct GgLayout {
+  static constexpr int TT = AB == 8 ? 4 : AB;
+  static constexpr int TW = AB == 8 ? 2 : 1;
+  // LDS row (within the stage) of activation tile tt / weight tile tw of wave wv
+  __device__ static int arow(int wv, int tt) { return AB == 8 ? ((wv >> 2) * 128 + tt * 32) : tt * 32; }
+  __device__ static int wtile(int wv, int tw) { return AB == 8 ? ((wv & 3) * 2 + tw) : wv; }
+  __device__ static int wrow(int wv, int tw) { return 32 * AB + 32 * wtile(wv, tw); }
+};
+
+template <bool GATEUP, int AB>
+__device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
+                                        uint32_t ring_lds) {
+  using L = GgLayout<AB>;
+  constexpr int TT = L::TT, TW = L::TW;
+  constexpr int NA = 2 * AB;    // activation loads (16 rows each) per stage
+  constexpr int NL = NA + 16;   // all loads per stage
+  constexpr int MAXJ = (NL + kGgWaves - 1) / kGgWaves;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int K = a.K;
+  const int nst = K / 32;
+  const int cnt = (NL - wv + kGgWaves - 1) / kGgWaves;  // loads this wave issues per stage
+
+  // this lane's source chunk for each of its loads (stage 0)
+  const int lr = lane >> 2;
+  const int lq = ring_slot(lr, lane & 3);
+  const uint16_t *src[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int i = wv + kGgWaves * j;
+    src[j] = a.act;
+    if (i < NA) {
+      const int R = i * 16 + lr;
+      const int row = t.row0 + min(R, t.nrows - 1);
+      const size_t s = GATEUP ? (size_t)(a.sorted_routes[row] / a.k) : (size_t)row;
+      src[j] = a.act + s * K + lq * 8;
+    } else if (i < NL) {
+      const int wr = (i - NA) * 16 + lr;
+      const uint16_t *w;
+      int n;
+      if (GATEUP) {  // 16-row groups alternate gate and up
+        w = ((wr >> 4) & 1) ? a.w1 : a.w0;
+        n = n0 + (wr >> 5) * 16 + (wr & 15);
+      } else {
+        w = a.w0;
+        n = min(n0 + wr, a.N - 1);
+      }
+      src[j] = w + ((size_t)t.e * a.N + n) * K + lq * 8;
+    }
+  }
+  auto issue = [&](int s, int slot) {
+    const uint32_t base = ring_lds + (uint32_t)(slot * kGgSlot);
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int i = wv + kGgWaves * j;
+      if (i < NL) dma16(src[j] + s * 32, base + (uint32_t)i * 1024u);
+    }
+  };
+
+  // reader: row (lane & 31) of a 32-row tile; reduction step ks reads chunk
+  // 2 ks + (lane >> 5) of the row's four, at its swizzled slot
+  const int rr = lane & 31, rh = lane >> 5;
+  const int lane_off[2] = {rr * 64 + ring_slot(rr & 15, rh) * 16,
+                           rr * 64 + ring_slot(rr & 15, 2 + rh) * 16};
+
+  f32x16 acc[TW][TT];
+#pragma unroll
+  for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+
+  wait_vm(0);
+  ring_barrier();  // every wave is done with the ring contents of the previous item
+#pragma unroll
+  for (int s = 0; s < kGgStages - 1; ++s)
+    if (s < nst) issue(s, s);
+  int slot = 0;
+  for (int s = 0; s < nst; ++s) {
+    // this wave's loads of stage s are done; later stages may stay in flight
+    wait_vm(cnt * min(kGgStages - 2, nst - 1 - s));
+    ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
+    const int ahead = s + kGgStages - 1;
+    if (ahead < nst) issue(ahead, slot == 0 ? kGgStages - 1 : slot - 1);
+    const uint8_t *buf = ring + slot * kGgSlot;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[TT], fw[TW];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        fa[tt] = *reinterpret_cast<const bf16x8 *>(buf + L::arow(wv, tt) * 64 + lane_off[ks]);
+#pragma unroll
+      for (int tw = 0; tw < TW; ++tw)
+        fw[tw] = *reinterpret_cast<const bf16x8 *>(buf + L::wrow(wv, tw) * 64 + lane_off[ks]);
+#pragma unroll
+      for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[tw][tt] = mfma32_bf16(fw[tw], fa[tt], acc[tw][tt]);
+    }
+    slot = slot == kGgStages - 1 ? 0 : slot + 1;
+  }
+
+  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int row = L::arow(wv, tt) + rr;
+    if (row < t.nrows) {
+#pragma unroll
+      for (int tw = 0; tw < TW; ++tw) {
+        const int wt = L::wtile(wv, tw);
+        if (GATEUP) {
+          // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int n = n0 + wt * 16 + g * 8 + rh * 4;
+            gg_store<true>(a, t.row0 + row, n, quad(acc[tw][tt], g), quad(acc[tw][tt], g + 2));
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wt * 32 + g * 8 + rh * 4;
+            if (n < a.N) gg_store<false>(a, t.row0 + row, n, quad(acc[tw][tt], g), f32x4{});
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kGgStages * kGgSlot];
+  // the queue head is passed through the idle ring between items
+  int *next_item = reinterpret_cast<int *>(ring);
+  const uint32_t ring_lds = lds_addr(ring);
+  constexpr int FEAT = GATEUP ? 128 : 256;  // output features per item
+  const int per_tile = (a.N + FEAT - 1) / FEAT;
+  const int total = *a.ntiles * per_tile;
+  for (;;) {
+    if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
+    __syncthreads();
+    const int it = *next_item;  // read before gg_item's first barrier; its loads overwrite it
+    if (it >= total) break;
+    const int ti = it / per_tile;
+    const int n0 = (it - ti * per_tile) * FEAT;
+    const Tile t = a.tiles[ti];
+    switch (t.pad) {
+      case 8: gg_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
+      case 4: gg_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
+      case 2: gg_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
+      default: gg_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+    }
+    // the ring (and the queue head in it) is rewritten only after every wave
+    // has passed this barrier
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream) {
+  if (stages & kStagePlan) {
+    hipLaunchKernelGGL(grouped_schedule_kernel, dim3(1), dim3(kGsThreads), 0, stream, L.offsets,
+                       L.E, L.sch, L.big);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  GgArgs g{};
+  g.k = L.k;
+  g.tiles = L.big;
+  g.ntiles = &L.sch->n_tiles;
+  if (stages & kStageGateUp) {
+    g.act = L.x;
+    g.sorted_routes = L.sorted_routes;
+    g.w0 = L.wg;
+    g.w1 = L.wu;
+    g.out = L.h;
+    g.N = L.f;
+    g.K = L.d;
+    g.counter = &L.sch->counter[0];
+    hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(L.num_cus), dim3(kGgThreads), 0, stream, g);
+  }
+  if (stages & kStageDown) {
+    g.act = L.h;
+    g.sorted_routes = nullptr;
+    g.w0 = L.wd;
+    g.w1 = nullptr;
+    g.out = L.y;
+    g.N = L.d;
+    g.K = L.f;
+    g.counter = &L.sch->counter[1];
+    hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(L.num_cus), dim3(kGgThreads), 0, stream,
+                       g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -44,7 +44,7 @@ struct FfnLaunch {
   int grid_cap;  // persistent workgroups per GEMM launch
   int num_cus;
 };
-hipError_t launch_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
+hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
 
 // fp8 grouped FFN: plan (schedule + per-row quantisation of x into qx, sx),
 // gate/up + SwiGLU (h in bf16), down (per-row quantisation of h, then GEMM).
