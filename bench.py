@@ -89,11 +89,14 @@ def traffic_from_profiles(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, r, n_experts: int):
-    """The fp64 oracle (expert-major, BLAS) on a bounded sample of the workload:
-    the fixed part (route table, combine) on all routes plus n_experts experts'
-    FFNs, extrapolated to all active experts."""
-    import numpy as np
+def cpu_baseline(wl, r, budget_s: float):
+    """The fp64 oracle (expert-major, BLAS) on a bounded sample of the workload.
+
+    The fixed part (route table, combine over all routes) is timed once; then
+    experts' FFNs are evaluated in chunks, in expert order, until about
+    budget_s seconds of CPU work or every active expert is done.  The time for
+    all active experts is extrapolated from the per-expert average.
+    """
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import moe as omoe
@@ -104,28 +107,30 @@ def cpu_baseline(wl, r, n_experts: int):
     fp8 = wl.dtype == "fp8"
     rt = route_table(r.topk_ids, r.route_mask, wl.E)
     active = [e for e in range(wl.E) if rt.counts[e] > 0]
-    subset = active[:max(1, min(n_experts, len(active)))]
-    cache = {e: synth.expert_weights(wl, e, 0) for e in subset}
-    src = cache.__getitem__
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
-        omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, src, wl.E, fp8=fp8, expert_subset=[])
+        omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, lambda e: None, wl.E,
+                             fp8=fp8, expert_subset=[])
         t_fixed = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, src, wl.E, fp8=fp8, expert_subset=subset)
-        t_sub = time.perf_counter() - t0
-    per_expert = max(t_sub - t_fixed, 0.0) / len(subset)
-    t_total = t_fixed + per_expert * len(active)
-    blas = [i.get("internal_api") for i in threadpool_info()]
-    _ = np
+        done, t_ffn = [], 0.0
+        while len(done) < len(active) and t_fixed + t_ffn < budget_s:
+            chunk = active[len(done):len(done) + 8]
+            cache = {e: synth.expert_weights(wl, e, 0) for e in chunk}  # generation not timed
+            t0 = time.perf_counter()
+            omoe.moe_ref_blocked(r.x, r.topk_ids, r.topk_w, r.route_mask, cache.__getitem__, wl.E,
+                                 fp8=fp8, expert_subset=chunk)
+            t_ffn += max(time.perf_counter() - t0 - t_fixed, 0.0)
+            done += chunk
+    t_total = t_fixed + t_ffn / len(done) * len(active)
+    blas = ",".join(sorted({str(i.get("internal_api")) for i in threadpool_info()}))
     return {
         "value": round(wl.T / t_total, 3),
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"moe_ref_blocked (fp64, BLAS {','.join(b for b in blas if b)}) on all {wl.T} tokens' "
-                   f"route table and combine plus the FFN of {len(subset)} of {len(active)} active experts "
-                   f"({t_sub:.1f} s measured, fixed part {t_fixed:.2f} s), extrapolated to all active experts"),
+        "sample": (f"moe_ref_blocked (fp64 numpy, BLAS {blas}): route table and combine over all "
+                   f"{wl.T} tokens plus the FFNs of {len(done)} of {len(active)} active experts "
+                   f"({t_fixed + t_ffn:.1f} s measured), extrapolated to all active experts"),
         "seconds_extrapolated": round(t_total, 2),
     }
 
@@ -136,8 +141,12 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-experts", type=int, default=32, help="experts in the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time spent on the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device-to-device copy of 1 GiB (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -174,6 +183,12 @@ def main():
     def step(ev=None):
         return run(*wargs, gate_up_events=ev)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -221,7 +236,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(wl, r, args.cpu_experts)
+        cpu = cpu_baseline(wl, r, args.cpu_seconds)
         log(f"cpu baseline: {cpu['value']} tokens/s ({cpu['sample']})")
 
     rec = {

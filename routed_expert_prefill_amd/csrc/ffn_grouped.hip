@@ -15,8 +15,8 @@
 // while compute-bound items of large experts run on others.
 //
 // Every item streams both operands through the LDS stage ring (ring.h): 256
-// weight rows and 32 x ablk activation rows per 32-element reduction stage,
-// kGgStages - 1 stages in flight while one is consumed.  MFMAs are 32x32x16
+// weight rows and 32 x ablk activation rows per 64-element reduction stage
+// (128-byte rows), with as many stages as the 160 KB of LDS holds (2 to 4).  MFMAs are 32x32x16
 // bf16; eight waves (two per SIMD, so one wave's matrix work covers the
 // other's barrier and LDS waits) each own 32-row weight tiles:
 //   ablk = 8 (256 rows): wave w takes weight tiles 2(w%4), 2(w%4)+1 and the
@@ -45,12 +45,16 @@ struct GgArgs {
 
 constexpr int kGgThreads = 512;
 constexpr int kGgWaves = kGgThreads / kWave;
-#ifndef MOE_GG_STAGES
-#define MOE_GG_STAGES 4
-#endif
-constexpr int kGgStages = MOE_GG_STAGES;  // ring slots: kGgStages - 1 stages in flight
 constexpr int kGgWRows = 256;
-constexpr int kGgSlot = (kBigRows + kGgWRows) * 64;  // bytes per ring slot (32 KB)
+constexpr int kGgRing = 160 * 1024;  // the whole LDS of a workgroup
+
+// Ring geometry of an item with 32 * AB activation rows: a stage is
+// (32 AB + 256) rows of 128 bytes, and the ring has as many slots as fit.
+template <int AB>
+struct GgRing {
+  static constexpr int kSlot = (32 * AB + kGgWRows) * 128;
+  static constexpr int kDepth = kGgRing / kSlot;
+};
 
 // ------------------------------------------------------------------ schedule
 
@@ -144,7 +148,7 @@ __device__ __forceinline__ f32x4 quad(const f32x16 &v, int g) {
 }
 
 // Operand tiles a wave multiplies for one stage: TT activation tiles and TW
-// weight tiles of 32 rows, for the two 16-wide reduction steps.
+// weight tiles of 32 rows, for the four 16-wide reduction steps.
 template <int AB>
 struct GgLayout {
   static constexpr int TT = AB == 8 ? 4 : AB;
@@ -160,30 +164,31 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
                                         uint32_t ring_lds) {
   using L = GgLayout<AB>;
   constexpr int TT = L::TT, TW = L::TW;
-  constexpr int NA = 2 * AB;    // activation loads (16 rows each) per stage
-  constexpr int NL = NA + 16;   // all loads per stage
+  constexpr int NA = 4 * AB;    // activation loads (8 rows each) per stage
+  constexpr int NL = NA + 32;   // all loads per stage
   constexpr int MAXJ = (NL + kGgWaves - 1) / kGgWaves;
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int K = a.K;
-  const int nst = K / 32;
+  const int nst = K / 64;
   const int cnt = (NL - wv + kGgWaves - 1) / kGgWaves;  // loads this wave issues per stage
 
-  // this lane's source chunk for each of its loads (stage 0)
-  const int lr = lane >> 2;
-  const int lq = ring_slot(lr, lane & 3);
+  // this lane's source chunk for each of its loads (stage 0): load i fills
+  // stage rows 8 i .. 8 i + 7; lane fills slot (lane & 7) of row 8 i + (lane >> 3)
+  const int lr = lane >> 3;
   const uint16_t *src[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int i = wv + kGgWaves * j;
+    const int lq = ring_slot(i * 8 + lr, lane & 7);  // the chunk that belongs in that slot
     src[j] = a.act;
     if (i < NA) {
-      const int R = i * 16 + lr;
+      const int R = i * 8 + lr;
       const int row = t.row0 + min(R, t.nrows - 1);
       const size_t s = GATEUP ? (size_t)(a.sorted_routes[row] / a.k) : (size_t)row;
       src[j] = a.act + s * K + lq * 8;
     } else if (i < NL) {
-      const int wr = (i - NA) * 16 + lr;
+      const int wr = (i - NA) * 8 + lr;
       const uint16_t *w;
       int n;
       if (GATEUP) {  // 16-row groups alternate gate and up
@@ -196,20 +201,23 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
       src[j] = w + ((size_t)t.e * a.N + n) * K + lq * 8;
     }
   }
+  constexpr int NS = GgRing<AB>::kDepth;
+  constexpr int SLOT = GgRing<AB>::kSlot;
   auto issue = [&](int s, int slot) {
-    const uint32_t base = ring_lds + (uint32_t)(slot * kGgSlot);
+    const uint32_t base = ring_lds + (uint32_t)(slot * SLOT);
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int i = wv + kGgWaves * j;
-      if (i < NL) dma16(src[j] + s * 32, base + (uint32_t)i * 1024u);
+      if (i < NL) dma16(src[j] + s * 64, base + (uint32_t)i * 1024u);
     }
   };
 
-  // reader: row (lane & 31) of a 32-row tile; reduction step ks reads chunk
-  // 2 ks + (lane >> 5) of the row's four, at its swizzled slot
+  // reader: row (lane & 31) of a 32-row tile; reduction step ks (16 elements)
+  // reads chunk 2 ks + (lane >> 5) of the row's eight, at its swizzled slot
   const int rr = lane & 31, rh = lane >> 5;
-  const int lane_off[2] = {rr * 64 + ring_slot(rr & 15, rh) * 16,
-                           rr * 64 + ring_slot(rr & 15, 2 + rh) * 16};
+  int lane_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) lane_off[ks] = rr * 128 + ring_slot(rr, 2 * ks + rh) * 16;
 
   f32x16 acc[TW][TT];
 #pragma unroll
@@ -222,31 +230,31 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
   wait_vm(0);
   ring_barrier();  // every wave is done with the ring contents of the previous item
 #pragma unroll
-  for (int s = 0; s < kGgStages - 1; ++s)
+  for (int s = 0; s < NS - 1; ++s)
     if (s < nst) issue(s, s);
   int slot = 0;
   for (int s = 0; s < nst; ++s) {
     // this wave's loads of stage s are done; later stages may stay in flight
-    wait_vm(cnt * min(kGgStages - 2, nst - 1 - s));
+    wait_vm(cnt * min(NS - 2, nst - 1 - s));
     ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
-    const int ahead = s + kGgStages - 1;
-    if (ahead < nst) issue(ahead, slot == 0 ? kGgStages - 1 : slot - 1);
-    const uint8_t *buf = ring + slot * kGgSlot;
+    const int ahead = s + NS - 1;
+    if (ahead < nst) issue(ahead, slot == 0 ? NS - 1 : slot - 1);
+    const uint8_t *buf = ring + slot * SLOT;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
       bf16x8 fa[TT], fw[TW];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
-        fa[tt] = *reinterpret_cast<const bf16x8 *>(buf + L::arow(wv, tt) * 64 + lane_off[ks]);
+        fa[tt] = *reinterpret_cast<const bf16x8 *>(buf + L::arow(wv, tt) * 128 + lane_off[ks]);
 #pragma unroll
       for (int tw = 0; tw < TW; ++tw)
-        fw[tw] = *reinterpret_cast<const bf16x8 *>(buf + L::wrow(wv, tw) * 64 + lane_off[ks]);
+        fw[tw] = *reinterpret_cast<const bf16x8 *>(buf + L::wrow(wv, tw) * 128 + lane_off[ks]);
 #pragma unroll
       for (int tw = 0; tw < TW; ++tw)
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[tw][tt] = mfma32_bf16(fw[tw], fa[tt], acc[tw][tt]);
     }
-    slot = slot == kGgStages - 1 ? 0 : slot + 1;
+    slot = slot == NS - 1 ? 0 : slot + 1;
   }
 
   // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
@@ -280,7 +288,7 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kGgStages * kGgSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kGgRing];
   // the queue head is passed through the idle ring between items
   int *next_item = reinterpret_cast<int *>(ring);
   const uint32_t ring_lds = lds_addr(ring);

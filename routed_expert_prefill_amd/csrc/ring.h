@@ -1,12 +1,14 @@
 // LDS stage ring fed by direct global->LDS loads (gfx950), shared by the
 // grouped GEMM kernels.
 //
-// A stage holds rows of 64 bytes (32 bf16 or 64 fp8 reduction elements).
-// Each wave instruction moves 16 rows x 64 bytes = 1 KB: lane i fetches 16
-// bytes and the hardware writes them to LDS at m0 + 16 i.  Inside a 16-row
-// block the four 16-byte chunks of row r are stored at slot ring_slot(r, q),
-// so 16 lanes reading one chunk of 16 consecutive rows touch 16 distinct
-// 16-byte slots of a 256-byte window (no bank conflicts).
+// A stage holds rows of 128 bytes (64 bf16 or 128 fp8 reduction elements):
+// full cache lines, which matters -- streaming weight rows from HBM 64 bytes
+// at a time (half lines) runs at ~3.6 TB/s on MI355X, whole 128-byte lines
+// at ~6.3 TB/s.  Each wave instruction moves 8 rows x 128 bytes = 1 KB: lane
+// i fetches 16 bytes and the hardware writes them to LDS at m0 + 16 i.  The
+// eight 16-byte chunks of row r are stored at slot ring_slot(r, q), so 16
+// lanes reading one chunk of 16 consecutive rows touch 16 distinct 16-byte
+// slots of a 256-byte window (no bank conflicts).
 #pragma once
 
 #include "common.h"
@@ -19,7 +21,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t *)p;
 }
 
-__device__ __forceinline__ int ring_slot(int r, int q) { return q ^ (((r >> 1) ^ (r >> 3)) & 3); }
+__device__ __forceinline__ int ring_slot(int r, int q) { return q ^ ((r >> 1) & 7); }
 
 // Direct global->LDS load of 16 bytes per lane to LDS byte address
 // lds_byte_addr + 16 * lane.  Written as inline assembly so the compiler's
@@ -50,7 +52,7 @@ __device__ __forceinline__ void wait_vm_imm() {
 }
 
 // Wait until at most n of this wave's vector-memory operations are
-// outstanding (n > 32 waits for all of them).
+// outstanding (n > 32 waits for all of them).  n is wave-uniform.
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
 #define MOE_WAIT_CASE(N) \
@@ -60,7 +62,10 @@ __device__ __forceinline__ void wait_vm(int n) {
     MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
     MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
     MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
-    MOE_WAIT_CASE(16) MOE_WAIT_CASE(18) MOE_WAIT_CASE(20) MOE_WAIT_CASE(24) MOE_WAIT_CASE(32)
+    MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
+    MOE_WAIT_CASE(21) MOE_WAIT_CASE(22) MOE_WAIT_CASE(23) MOE_WAIT_CASE(24) MOE_WAIT_CASE(25)
+    MOE_WAIT_CASE(26) MOE_WAIT_CASE(27) MOE_WAIT_CASE(28) MOE_WAIT_CASE(29) MOE_WAIT_CASE(30)
+    MOE_WAIT_CASE(31) MOE_WAIT_CASE(32)
 #undef MOE_WAIT_CASE
     default:
       wait_vm_imm<0>();

@@ -1,18 +1,109 @@
-"""Print a per-kernel table (calls, total, average, share) from a rocprofv3
-kernel-trace database: python -m routed_expert_prefill_amd.profiling <run_results.db>."""
+"""Summaries of rocprofv3 output (kernel traces and counter runs).
+
+  python -m routed_expert_prefill_amd.profiling trace <run_results.db>
+      per-kernel table (calls, total, average, share) of a --kernel-trace run
+  python -m routed_expert_prefill_amd.profiling traffic --fetch <csv> --write <csv>
+          --kernel <name prefix> --workload <name> --out <json>
+      HBM bytes per launch of one kernel from a FETCH_SIZE run and a
+      WRITE_SIZE run (--output-format csv), each scaled by what the same
+      counter reads for the 1 GiB device copy that bench.py --copy-calibration
+      runs in the same process; records the kernel source hash bench.py checks.
+"""
+import argparse
+import csv
+import json
+import os
 import sqlite3
 import sys
 
 
-def main(db):
+def trace_table(db):
     c = sqlite3.connect(db)
     rows = c.execute("select name, total_calls, total_duration, average, percentage "
                      "from top_kernels order by total_duration desc").fetchall()
-    print("| kernel | calls | total (us) | average (us) | share |")
-    print("|---|---|---|---|---|")
+    out = ["| kernel | calls | total (us) | average (us) | share |", "|---|---|---|---|---|"]
     for name, calls, tot, avg, pct in rows:
-        print(f"| `{name.split('(')[0]}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.2f}% |")
+        out.append(f"| `{name.split('(')[0]}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.2f}% |")
+    return "\n".join(out)
+
+
+def _per_kernel(csv_path, counter):
+    vals = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def _match(vals, prefix):
+    hits = [v for k, v in vals.items() if k.startswith(prefix)]
+    if not hits:
+        raise SystemExit(f"no dispatch of a kernel starting with {prefix!r}")
+    flat = [x for v in hits for x in v]
+    return sum(flat) / len(flat), len(flat)
+
+
+def _copy_kib(vals):
+    # the 1 GiB copy is the largest single dispatch of a copy kernel in the run
+    best = None
+    for name, v in vals.items():
+        if "copy" in name.lower() or "elementwise" in name.lower():
+            m = max(v)
+            best = m if best is None or m > best else best
+    if best is None:
+        raise SystemExit("no copy kernel in the counter run (run bench.py with --copy-calibration)")
+    return best
+
+
+def traffic(args):
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    fetch = _per_kernel(args.fetch, "FETCH_SIZE")
+    write = _per_kernel(args.write, "WRITE_SIZE")
+    f_kib, nf = _match(fetch, args.kernel)
+    w_kib, nw = _match(write, args.kernel)
+    gib_kib = (1 << 30) / 1024.0
+    f_scale = gib_kib / _copy_kib(fetch)   # copy reads exactly 1 GiB
+    w_scale = gib_kib / _copy_kib(write)   # and writes exactly 1 GiB
+    rec = {
+        "kernel": args.kernel,
+        "workload": args.workload,
+        "fetch_kib_raw": round(f_kib, 1),
+        "write_kib_raw": round(w_kib, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "dispatches": [nf, nw],
+        "bytes_per_launch": int(round((f_kib * f_scale + w_kib * w_scale) * 1024)),
+        "source_sha": bench.source_hash(),
+    }
+    with open(args.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def main(argv=None):
+    argv = list(sys.argv[1:] if argv is None else argv)
+    if argv and argv[0].endswith(".db"):
+        argv = ["trace"] + argv  # older form: a bare database path
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    f = sub.add_parser("traffic")
+    f.add_argument("--fetch", required=True)
+    f.add_argument("--write", required=True)
+    f.add_argument("--kernel", required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(trace_table(a.db))
+    else:
+        traffic(a)
 
 
 if __name__ == "__main__":
-    main(sys.argv[1])
+    main()
