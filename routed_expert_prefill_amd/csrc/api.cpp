@@ -29,17 +29,12 @@ int num_cus_current_device() {
   return cus;
 }
 
-// Persistent workgroups per GEMM launch: a few per compute unit.
-int grid_cap_for_current_device() {
-  const int cus = num_cus_current_device();
-#ifndef MOE_GRID_PER_CU
-#define MOE_GRID_PER_CU 4
-#endif
-  return cus * MOE_GRID_PER_CU;
-}
+// Workgroups of a row-quantisation launch: four per compute unit, each
+// looping over rows.
+int grid_cap_for_current_device() { return num_cus_current_device() * 4; }
 
 struct FfnLayout {
-  size_t sched, skinny, fat, big, h, qx, sx, qh, sh, total;
+  size_t sched, tiles, h, qx, sx, qh, sh, total;
 };
 
 bool ffn_desc_status(const moe_ffn_desc *d, int *st) {
@@ -83,12 +78,8 @@ FfnLayout ffn_layout(const moe_ffn_desc *d) {
   size_t off = 0;
   L.sched = off;
   off += align_up(sizeof(moe::Schedule));
-  L.skinny = off;
-  off += align_up(sizeof(moe::Tile) * (size_t)d->E);
-  L.fat = off;
-  off += align_up(sizeof(moe::Tile) * (R / moe::kFatRows + (size_t)d->E));
-  L.big = off;
-  off += align_up(sizeof(moe::Tile) * (R / moe::kBigRows + (size_t)d->E));
+  L.tiles = off;  // at most R / 256 full tiles plus one remainder per expert
+  off += align_up(sizeof(moe::Tile) * (R / moe::kTileRows + (size_t)d->E));
   L.h = off;
   off += align_up(R * (size_t)d->f * 2);
   if (fp8) {
@@ -182,7 +173,6 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
   char *ws = static_cast<char *>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = desc->T * desc->k;
-  const int cap = grid_cap_for_current_device();
   if (!fp8) {
     moe::FfnLaunch L{};
     L.x = static_cast<const uint16_t *>(x);
@@ -194,9 +184,7 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
     L.y = y;
     L.h = reinterpret_cast<uint16_t *>(ws + lay.h);
     L.sch = reinterpret_cast<moe::Schedule *>(ws + lay.sched);
-    L.skinny = reinterpret_cast<moe::Tile *>(ws + lay.skinny);
-    L.fat = reinterpret_cast<moe::Tile *>(ws + lay.fat);
-    L.big = reinterpret_cast<moe::Tile *>(ws + lay.big);
+    L.tiles = reinterpret_cast<moe::Tile *>(ws + lay.tiles);
     L.num_cus = num_cus_current_device();
     L.T = desc->T;
     L.k = desc->k;
@@ -204,7 +192,6 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
     L.d = desc->d;
     L.f = desc->f;
     L.R = R;
-    L.grid_cap = cap;
     return status_from(moe::launch_grouped_ffn_bf16(L, stages, s));
   }
   moe::FfnLaunchFp8 L{};
@@ -224,9 +211,7 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
   L.qh = reinterpret_cast<uint8_t *>(ws + lay.qh);
   L.sh = reinterpret_cast<float *>(ws + lay.sh);
   L.sch = reinterpret_cast<moe::Schedule *>(ws + lay.sched);
-  L.skinny = reinterpret_cast<moe::Tile *>(ws + lay.skinny);
-  L.fat = reinterpret_cast<moe::Tile *>(ws + lay.fat);
-  L.big = reinterpret_cast<moe::Tile *>(ws + lay.big);
+  L.tiles = reinterpret_cast<moe::Tile *>(ws + lay.tiles);
   L.num_cus = num_cus_current_device();
   L.T = desc->T;
   L.k = desc->k;
@@ -234,7 +219,7 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
   L.d = desc->d;
   L.f = desc->f;
   L.R = R;
-  L.grid_cap = cap;
+  L.grid_cap = grid_cap_for_current_device();
   return status_from(moe::launch_ffn_fp8(L, stages, s));
 }
 

@@ -14,34 +14,24 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
-// One row-block of one expert: rows [row0, row0 + nrows) of the expert-sorted
-// route order all belong to expert e.
+// One row tile of one expert: rows [row0, row0 + nrows) of the expert-sorted
+// route order all belong to expert e.  ablk = row capacity / 32 (1, 2, 4 or
+// 8): an expert's segment is cut into full tiles of kTileRows rows and one
+// remainder tile of the smallest capacity (32, 64, 128 or 256) that holds it.
 struct Tile {
   int e;
   int row0;
   int nrows;
-  int pad;
+  int ablk;
 };
 
-// Tile classes.  An expert's segment of n rows is cut into full big tiles of
-// kBigRows rows; the remainder r becomes one big tile if r > kFatRows, one fat
-// tile if kSkinnyMaxRows < r <= kFatRows, and one skinny tile otherwise.
-//  skinny: <= 32 rows, weights streamed straight into MFMA operand registers;
-//  fat:    <= 128 rows, both operands staged through LDS by the waves;
-//  big:    <= 256 rows, both operands streamed into an LDS ring by direct
-//          global->LDS loads.
-constexpr int kSkinnyMaxRows = 32;
-constexpr int kFatRows = 128;
-constexpr int kBigRows = 256;
+constexpr int kTileRows = 256;
 
 // Layout of the schedule at the start of the grouped-FFN workspace.
 struct Schedule {
-  int n_skinny;
-  int n_fat;
-  int n_big;
-  int n_tiles;     // all tiles of the single ordered list (bf16 path)
+  int n_tiles;     // entries of the tile list, tallest capacity first
   int counter[2];  // work-queue heads of the gate/up and down kernels
-  int pad[58];     // keeps the tile arrays 256-byte aligned
+  int pad[61];     // keeps the tile list 256-byte aligned
 };
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l

@@ -1,469 +1,332 @@
-// Grouped gate/up (+ fused SwiGLU) and down GEMMs, E4M3 weights with one fp32
-// scale per 128x128 block and E4M3 activations with one fp32 scale per row.
+// Persistent grouped GEMM for the fp8 routed-MoE FFN: E4M3 weights with one
+// fp32 scale per 128 x 128 block, E4M3 activations with one fp32 scale per
+// row (x per token, h per routed row).
 //
-// Same schedule and tile classes as the bf16 path.  One 16x16x128 MFMA covers
-// exactly one 128-wide scale block of the reduction, so each block's partial
-// product P is formed with a zero accumulator and folded in as
-//   acc += s_w[n/128, kb] * P
-// (the 16 output features of one MFMA lie in one 128-row scale block).  The
-// per-row activation scale is constant along the reduction and multiplies the
-// accumulator once in the epilogue.  Between the GEMMs, h is written in bf16
-// and quantised per row by the row-quantisation kernel.
+// Same tile list, work queue and LDS stage ring as the bf16 kernels
+// (ffn_grouped.hip, ring.h).  A ring row is 128 bytes = 128 fp8 reduction
+// elements = one weight scale block, so each stage's partial product P (two
+// chained 32x32x64 fp8 MFMAs from zero) is folded into the fp32 accumulator
+// once: acc += s_w[n / 128][stage] * P.  The activation row scale is constant
+// along the reduction and multiplies the accumulator in the epilogue.  Items
+// carry 128 weight rows (gate/up: 64 features of both matrices, interleaved
+// in 16-row groups; down: 128 features), which keeps the fold of a wave in
+// proportion to its MFMAs.  Between the projections h is written in bf16 and
+// then quantised per row.
 #include "kernels.h"
+#include "ring.h"
 
 namespace moe {
 
-struct GemmArgs8 {
+struct Gg8Args {
   const uint8_t *act;            // gate/up: qx [T, K]; down: qh [R, K]
   const float *act_scale;        // gate/up: sx [T]; down: sh [R]
-  const int32_t *sorted_routes;  // gate/up only
+  const int32_t *sorted_routes;  // gate/up: token of sorted row i is sorted_routes[i] / k
   int k;
-  const uint8_t *w0, *w1;  // [E, N, K] codes (w1: up, gate/up only)
-  const float *s0, *s1;    // [E, N/128, K/128]
+  const uint8_t *w0, *w1;  // [E, N, K] codes: gate (or down), up
+  const float *s0, *s1;    // [E, N / 128, K / 128] block scales of w0, w1
   void *out;               // gate/up: h bf16 [R, N]; down: y fp32 [R, N]
-  int N, K;
+  int N, K;                // K <= 16384: a lane pair holds the K / 128 scales of a row
   const Tile *tiles;
   const int *ntiles;
+  int *counter;
 };
 
-__device__ __forceinline__ i32x8 load_i32x8(const uint8_t *p) {
-  const i32x4 lo = *reinterpret_cast<const i32x4 *>(p);
-  const i32x4 hi = *reinterpret_cast<const i32x4 *>(p + 16);
+constexpr int kG8Threads = 512;
+constexpr int kG8Waves = kG8Threads / kWave;
+constexpr int kG8WRows = 128;
+constexpr int kG8Ring = 160 * 1024;
+
+template <int AB>
+struct G8Ring {
+  static constexpr int kSlot = (32 * AB + kG8WRows) * 128;
+  static constexpr int kDepth = (kG8Ring / kSlot) < 8 ? (kG8Ring / kSlot) : 8;
+};
+
+// Wave wv multiplies TT activation tiles by TW weight tiles (32 rows each).
+// An item has 4 weight tiles and AB activation tiles; with AB = 1 only waves
+// 0-3 have a pair (waves 4-7 still load).
+template <int AB>
+struct G8Layout {
+  static constexpr int TT = AB >= 4 ? 2 : 1;
+  static constexpr int TW = AB == 8 ? 2 : 1;
+  __device__ static bool active(int wv) { return AB > 1 || wv < 4; }
+  __device__ static int atile(int wv, int tt) {
+    return AB == 8 ? (wv >> 1) * 2 + tt : AB == 4 ? (wv >> 2) * 2 + tt : AB == 2 ? (wv >> 2) : 0;
+  }
+  __device__ static int wtile(int wv, int tw) { return AB == 8 ? (wv & 1) * 2 + tw : (wv & 3); }
+};
+
+// 32x32x64 E4M3 x E4M3 MFMA with unit block exponents (E8M0 127 = 2^0).  Lane
+// l supplies row l % 32 of its operand and 32 reduction elements; both
+// operands are read with the same lane -> element map, so the sum covers the
+// 64 elements of the step whatever order the unit takes them in.  Result
+// layout as for the bf16 32x32 shape.
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 lds_i32x8(const uint8_t *p0, const uint8_t *p1) {
+  const i32x4 lo = *reinterpret_cast<const i32x4 *>(p0);
+  const i32x4 hi = *reinterpret_cast<const i32x4 *>(p1);
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ void fold(f32x4 &acc, float s, const f32x4 &p) {
-  acc[0] = __builtin_fmaf(s, p[0], acc[0]);
-  acc[1] = __builtin_fmaf(s, p[1], acc[1]);
-  acc[2] = __builtin_fmaf(s, p[2], acc[2]);
-  acc[3] = __builtin_fmaf(s, p[3], acc[3]);
+__device__ __forceinline__ f32x4 quad_scaled(const f32x16 &v, int g, float s) {
+  return f32x4{v[4 * g] * s, v[4 * g + 1] * s, v[4 * g + 2] * s, v[4 * g + 3] * s};
 }
 
-template <bool GATEUP>
-__device__ __forceinline__ void store_out8(const GemmArgs8 &a, int row, int n, float rs,
-                                           const f32x4 &g, const f32x4 &u) {
-  if constexpr (GATEUP) {
-    uint32_t lo = (uint32_t)f32_to_bf16_bits(swiglu(g[0] * rs, u[0] * rs)) |
-                  ((uint32_t)f32_to_bf16_bits(swiglu(g[1] * rs, u[1] * rs)) << 16);
-    uint32_t hi = (uint32_t)f32_to_bf16_bits(swiglu(g[2] * rs, u[2] * rs)) |
-                  ((uint32_t)f32_to_bf16_bits(swiglu(g[3] * rs, u[3] * rs)) << 16);
-    uint2 v;
-    v.x = lo;
-    v.y = hi;
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)row * a.N + n) = v;
-  } else {
-    const f32x4 v = {g[0] * rs, g[1] * rs, g[2] * rs, g[3] * rs};
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (size_t)row * a.N + n) = v;
-  }
+// Scale of reduction block s (uniform) from the pair (lo: block lane, hi:
+// block 64 + lane) that the lanes of a wave hold.
+__device__ __forceinline__ float block_scale(float lo, float hi, int s) {
+  const float v = s < 64 ? lo : hi;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s & 63));
 }
 
-// ------------------------------------------------------------------ schedule
-//
-// Tiles of the fp8 path: each expert's segment is cut into 128-row fat tiles
-// and a remainder (a fat tile if it holds more than 32 rows, else a skinny
-// tile), written to two lists.
-
-constexpr int kSchedThreads = 256;
-
-__device__ int block_excl_scan(int v, int *total, int *buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int a = (t >= off) ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += a;
-    __syncthreads();
-  }
-  const int incl = buf[t];
-  *total = buf[kSchedThreads - 1];
-  __syncthreads();
-  return incl - v;
-}
-
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *__restrict__ offsets,
-                                                                 int E, Schedule *sch,
-                                                                 Tile *__restrict__ skinny,
-                                                                 Tile *__restrict__ fat,
-                                                                 Tile *__restrict__ big) {
-  __shared__ int buf[kSchedThreads];
-  const int e = threadIdx.x;
-  int n = 0, row0 = 0;
-  if (e < E) {
-    row0 = offsets[e];
-    n = offsets[e + 1] - row0;
-  }
-  // full big tiles, then one tile for the remainder chosen by its size
-  int nb = 0, rem = n;
-  if (big != nullptr) {
-    nb = n / kBigRows;
-    rem = n - nb * kBigRows;
-    if (rem > kFatRows) {
-      ++nb;
-      rem = 0;
-    }
-  }
-  int nf = 0;
-  if (big == nullptr) {  // no big class: cut into fat tiles
-    nf = rem / kFatRows;
-    rem -= nf * kFatRows;
-  }
-  if (rem > kSkinnyMaxRows) {
-    ++nf;
-    rem = -rem;  // marks "remainder is one fat tile"
-  }
-  const int cs = rem > 0 ? 1 : 0;
-  int tot_s, tot_f, tot_b;
-  const int ps = block_excl_scan(cs, &tot_s, buf);
-  const int pf = block_excl_scan(nf, &tot_f, buf);
-  const int pb = block_excl_scan(nb, &tot_b, buf);
-  int r = row0;
-  for (int i = 0; i < nb; ++i) {
-    Tile t;
-    t.e = e;
-    t.row0 = r;
-    t.nrows = min(kBigRows, row0 + n - r);
-    t.pad = 0;
-    big[pb + i] = t;
-    r += t.nrows;
-  }
-  for (int i = 0; i < nf; ++i) {
-    Tile t;
-    t.e = e;
-    t.row0 = r;
-    t.nrows = min(kFatRows, row0 + n - r);
-    t.pad = 0;
-    fat[pf + i] = t;
-    r += t.nrows;
-  }
-  if (cs) {
-    Tile t;
-    t.e = e;
-    t.row0 = r;
-    t.nrows = rem;
-    t.pad = 0;
-    skinny[ps] = t;
-  }
-  if (e == 0) {
-    sch->n_skinny = tot_s;
-    sch->n_fat = tot_f;
-    sch->n_big = tot_b;
-  }
-}
-
-// ------------------------------------------------------------------ skinny tiles
-
-constexpr int kSk8Threads = 256;
-constexpr int kSk8Waves = kSk8Threads / kWave;
-template <bool GATEUP>
-constexpr int sk8_tn() { return GATEUP ? 2 : 4; }
-template <bool GATEUP>
-constexpr int sk8_feat() { return kSk8Waves * sk8_tn<GATEUP>() * 16; }
-
-template <bool GATEUP, int TM>
-__device__ __forceinline__ void skinny8_item(const GemmArgs8 &a, const Tile &t, int n_item0) {
-  constexpr int TN = sk8_tn<GATEUP>();
-  constexpr int NB = GATEUP ? 2 : 1;
+template <bool GATEUP, int AB>
+__device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0, uint8_t *ring,
+                                        uint32_t ring_lds) {
+  using L = G8Layout<AB>;
+  constexpr int TT = L::TT, TW = L::TW;
+  constexpr int NA = 4 * AB;             // activation loads (8 rows each) per stage
+  constexpr int NL = NA + kG8WRows / 8;  // all loads per stage
+  constexpr int MAXJ = (NL + kG8Waves - 1) / kG8Waves;
+  constexpr int NS = G8Ring<AB>::kDepth;
+  constexpr int SLOT = G8Ring<AB>::kSlot;
   const int lane = lane_id();
-  const int wv = threadIdx.x / kWave;
-  const int m = lane & 15, q = lane >> 4;
-  const int n_w = n_item0 + wv * TN * 16;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int K = a.K;
-  const int KB = K / 128;
-  if (n_w >= a.N) return;
+  const int nst = K / 128;
+  const int cnt = (NL - wv + kG8Waves - 1) / kG8Waves;  // loads this wave issues per stage
 
-  const uint8_t *arow[TM];
-  float rs[TM];
+  // load i fills stage rows 8 i .. 8 i + 7; this lane fills slot (lane & 7)
+  // of row 8 i + (lane >> 3) with the chunk that belongs there
+  const int lr = lane >> 3;
+  const uint8_t *src[MAXJ];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int r = min(tm * 16 + m, t.nrows - 1);
-    const int i = t.row0 + r;
-    const size_t src = GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i;
-    arow[tm] = a.act + src * K + q * 32;
-    rs[tm] = a.act_scale[src];
-  }
-  const uint8_t *wrow[NB][TN];
-  const float *srow[NB][TN];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int n = n_w + tn * 16;
-      wrow[b][tn] = (b == 0 ? a.w0 : a.w1) + ((size_t)t.e * a.N + n + m) * K + q * 32;
-      srow[b][tn] = (b == 0 ? a.s0 : a.s1) + ((size_t)t.e * (a.N / 128) + n / 128) * KB;
+  for (int j = 0; j < MAXJ; ++j) {
+    const int i = wv + kG8Waves * j;
+    const int lq = ring_slot(i * 8 + lr, lane & 7);
+    src[j] = a.act;
+    if (i < NA) {
+      const int row = t.row0 + min(i * 8 + lr, t.nrows - 1);
+      const size_t s = GATEUP ? (size_t)(a.sorted_routes[row] / a.k) : (size_t)row;
+      src[j] = a.act + s * K + lq * 16;
+    } else if (i < NL) {
+      const int wr = (i - NA) * 8 + lr;
+      const uint8_t *w;
+      int n;
+      if (GATEUP) {  // 16-row groups alternate gate and up
+        w = ((wr >> 4) & 1) ? a.w1 : a.w0;
+        n = n0 + (wr >> 5) * 16 + (wr & 15);
+      } else {
+        w = a.w0;
+        n = min(n0 + wr, a.N - 1);
+      }
+      src[j] = w + ((size_t)t.e * a.N + n) * K + lq * 16;
     }
-
-  f32x4 acc[NB][TN][TM];
+  }
+  auto issue = [&](int s, int slot) {
+    const uint32_t base = ring_lds + (uint32_t)(slot * SLOT);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) acc[b][tn][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  i32x8 wA[NB][TN], xA[TM], wB[NB][TN], xB[TM];
-  auto load = [&](i32x8(&w)[NB][TN], i32x8(&x)[TM], int kb) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) w[b][tn] = load_i32x8(wrow[b][tn] + kb * 128);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) x[tm] = load_i32x8(arow[tm] + kb * 128);
+    for (int j = 0; j < MAXJ; ++j) {
+      const int i = wv + kG8Waves * j;
+      if (i < NL) dma16(src[j] + s * 128, base + (uint32_t)i * 1024u);
+    }
   };
-  auto compute = [&](i32x8(&w)[NB][TN], i32x8(&x)[TM], int kb) {
+
+  // the item's weight rows all lie in one 128-row scale block
+  const int KB = nst;
+  const size_t srow = ((size_t)t.e * (a.N / 128) + n0 / 128) * KB;
+  float sc0[2], sc1[2];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+  for (int h = 0; h < 2; ++h) {
+    const int kb = lane + 64 * h;
+    sc0[h] = kb < KB ? a.s0[srow + kb] : 0.f;
+    sc1[h] = (GATEUP && kb < KB) ? a.s1[srow + kb] : 0.f;
+  }
+
+  // reader: row (lane & 31) of a 32-row tile; 64-element step ks takes the
+  // 32 bytes of chunks 4 ks + 2 (lane >> 5) and 4 ks + 2 (lane >> 5) + 1
+  const int rr = lane & 31, rh = lane >> 5;
+  int off0[2], off1[2];
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const float s = srow[b][tn][kb];
+  for (int ks = 0; ks < 2; ++ks) {
+    off0[ks] = rr * 128 + ring_slot(rr, 4 * ks + 2 * rh) * 16;
+    off1[ks] = rr * 128 + ring_slot(rr, 4 * ks + 2 * rh + 1) * 16;
+  }
+
+  f32x16 acc[TW][TT];
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const f32x4 p = mfma_fp8(w[b][tn], x[tm], f32x4{0.f, 0.f, 0.f, 0.f});
-          fold(acc[b][tn][tm], s, p);
+  for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+  const bool on = L::active(wv);
+
+  wait_vm(0);
+  ring_barrier();  // every wave is done with the ring contents of the previous item
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s, s);
+  int slot = 0;
+  for (int s = 0; s < nst; ++s) {
+    wait_vm(cnt * min(NS - 2, nst - 1 - s));
+    ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
+    const int ahead = s + NS - 1;
+    if (ahead < nst) issue(ahead, slot == 0 ? NS - 1 : slot - 1);
+    if (on) {
+      const uint8_t *buf = ring + slot * SLOT;
+      const float sg = block_scale(sc0[0], sc0[1], s);
+      const float su = GATEUP ? block_scale(sc1[0], sc1[1], s) : sg;
+      i32x8 fa[TT][2], fw[TW][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const uint8_t *r = buf + L::atile(wv, tt) * 32 * 128;
+          fa[tt][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
+        }
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+          const uint8_t *r = buf + (32 * AB + L::wtile(wv, tw) * 32) * 128;
+          fw[tw][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
         }
       }
-  };
-
-  load(wA, xA, 0);
-  for (int kb = 0; kb < KB; kb += 2) {
-    if (kb + 1 < KB) load(wB, xB, kb + 1);
-    compute(wA, xA, kb);
-    if (kb + 2 < KB) load(wA, xA, kb + 2);
-    if (kb + 1 < KB) compute(wB, xB, kb + 1);
+#pragma unroll
+      for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          f32x16 p;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) p[j] = 0.f;
+          p = mfma32_fp8(fw[tw][0], fa[tt][0], p);
+          p = mfma32_fp8(fw[tw][1], fa[tt][1], p);
+          // gate/up: registers 0-7 hold gate rows of the tile, 8-15 up rows
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            acc[tw][tt][j] = __builtin_fmaf((GATEUP && j >= 8) ? su : sg, p[j], acc[tw][tt][j]);
+        }
+    }
+    slot = slot == NS - 1 ? 0 : slot + 1;
   }
 
+  if (!on) return;
+  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int row = tm * 16 + m;
+  for (int tt = 0; tt < TT; ++tt) {
+    const int row = L::atile(wv, tt) * 32 + rr;
     if (row < t.nrows) {
+      const int i = t.row0 + row;
+      const float rs = a.act_scale[GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i];
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int n = n_w + tn * 16 + q * 4;
-        store_out8<GATEUP>(a, t.row0 + row, n, rs[tm], acc[0][tn][tm], acc[NB - 1][tn][tm]);
-      }
-    }
-  }
-}
-
-template <bool GATEUP>
-__global__ __launch_bounds__(kSk8Threads) void skinny8_kernel(GemmArgs8 a) {
-  const int per_tile = (a.N + sk8_feat<GATEUP>() - 1) / sk8_feat<GATEUP>();
-  const int total = *a.ntiles * per_tile;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int ti = it / per_tile;
-    const int j = it - ti * per_tile;
-    const Tile t = a.tiles[ti];
-    if (t.nrows <= 16)
-      skinny8_item<GATEUP, 1>(a, t, j * sk8_feat<GATEUP>());
-    else
-      skinny8_item<GATEUP, 2>(a, t, j * sk8_feat<GATEUP>());
-  }
-}
-
-// ------------------------------------------------------------------ fat tiles
-
-constexpr int kFt8Threads = 256;
-constexpr int kFt8BN = 128;
-constexpr int kFt8KT = 128;          // one scale block per LDS stage
-constexpr int kFt8Ld = kFt8KT + 16;  // padded LDS row (bytes)
-
-template <bool GATEUP>
-__global__ __launch_bounds__(kFt8Threads) void fat8_kernel(GemmArgs8 a) {
-  constexpr int NB = GATEUP ? 2 : 1;
-  constexpr int BM = kFatRows;
-  constexpr int TN = 4, TM = 4;
-  constexpr int CH = kFt8KT / 16;                  // 16-byte chunks per row per stage
-  constexpr int LOADS = BM * CH / kFt8Threads;     // 4
-  __shared__ __attribute__((aligned(16))) uint8_t sW[NB][kFt8BN][kFt8Ld];
-  __shared__ __attribute__((aligned(16))) uint8_t sX[BM][kFt8Ld];
-
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wv = tid / kWave;
-  const int wf = wv & 1, wt = wv >> 1;
-  const int m = lane & 15, q = lane >> 4;
-  const int K = a.K;
-  const int KB = K / 128;
-  const int per_tile = a.N / kFt8BN;
-  const int total = *a.ntiles * per_tile;
-
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int ti = it / per_tile;
-    const int n0 = (it - ti * per_tile) * kFt8BN;
-    const Tile t = a.tiles[ti];
-
-    const uint8_t *xsrc[LOADS];
-    const uint8_t *wsrc[NB][LOADS];
-    int lrow[LOADS], lcol[LOADS];
+      for (int tw = 0; tw < TW; ++tw) {
+        const int wt = L::wtile(wv, tw);
+        if (GATEUP) {
+          // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
 #pragma unroll
-    for (int c = 0; c < LOADS; ++c) {
-      const int chunk = tid + c * kFt8Threads;
-      lrow[c] = chunk / CH;
-      lcol[c] = (chunk % CH) * 16;
-      const int r = min(lrow[c], t.nrows - 1);
-      const int i = t.row0 + r;
-      const size_t src = GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i;
-      xsrc[c] = a.act + src * K + lcol[c];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        wsrc[b][c] = (b == 0 ? a.w0 : a.w1) + ((size_t)t.e * a.N + n0 + lrow[c]) * K + lcol[c];
-    }
-    // the 128 output features of this item share one scale row per matrix
-    const float *srow[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      srow[b] = (b == 0 ? a.s0 : a.s1) + ((size_t)t.e * (a.N / 128) + n0 / 128) * KB;
-    float rs[TM];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int r = min(wt * 64 + tm * 16 + m, t.nrows - 1);
-      const int i = t.row0 + r;
-      const size_t src = GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i;
-      rs[tm] = a.act_scale[src];
-    }
-
-    f32x4 acc[NB][TN][TM];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) acc[b][tn][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    i32x4 rx[LOADS], rw[NB][LOADS];
-    auto gload = [&](int kb) {
-#pragma unroll
-      for (int c = 0; c < LOADS; ++c) {
-        rx[c] = *reinterpret_cast<const i32x4 *>(xsrc[c] + kb * 128);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) rw[b][c] = *reinterpret_cast<const i32x4 *>(wsrc[b][c] + kb * 128);
-      }
-    };
-    gload(0);
-    for (int kb = 0; kb < KB; ++kb) {
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < LOADS; ++c) {
-        *reinterpret_cast<i32x4 *>(&sX[lrow[c]][lcol[c]]) = rx[c];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) *reinterpret_cast<i32x4 *>(&sW[b][lrow[c]][lcol[c]]) = rw[b][c];
-      }
-      __syncthreads();
-      if (kb + 1 < KB) gload(kb + 1);
-      float s[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) s[b] = srow[b][kb];
-      i32x8 fw[NB][TN], fx[TM];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) fw[b][tn] = load_i32x8(&sW[b][wf * 64 + tn * 16 + m][q * 32]);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) fx[tm] = load_i32x8(&sX[wt * 64 + tm * 16 + m][q * 32]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            const f32x4 p = mfma_fp8(fw[b][tn], fx[tm], f32x4{0.f, 0.f, 0.f, 0.f});
-            fold(acc[b][tn][tm], s[b], p);
+          for (int g = 0; g < 2; ++g) {
+            const f32x4 gv = quad_scaled(acc[tw][tt], g, rs);
+            const f32x4 uv = quad_scaled(acc[tw][tt], g + 2, rs);
+            uint2 v;
+            v.x = (uint32_t)f32_to_bf16_bits(swiglu(gv[0], uv[0])) |
+                  ((uint32_t)f32_to_bf16_bits(swiglu(gv[1], uv[1])) << 16);
+            v.y = (uint32_t)f32_to_bf16_bits(swiglu(gv[2], uv[2])) |
+                  ((uint32_t)f32_to_bf16_bits(swiglu(gv[3], uv[3])) << 16);
+            const int n = n0 + wt * 16 + g * 8 + rh * 4;
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)i * a.N + n) = v;
           }
-    }
-
+        } else {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int row = wt * 64 + tm * 16 + m;
-      if (row < t.nrows) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = n0 + wf * 64 + tn * 16 + q * 4;
-          store_out8<GATEUP>(a, t.row0 + row, n, rs[tm], acc[0][tn][tm], acc[NB - 1][tn][tm]);
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wt * 32 + g * 8 + rh * 4;
+            if (n < a.N)
+              *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (size_t)i * a.N + n) =
+                  quad_scaled(acc[tw][tt], g, rs);
+          }
         }
       }
     }
   }
 }
 
-// ------------------------------------------------------------------ host side
-
-hipError_t launch_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *skinny, Tile *fat,
-                           Tile *big, hipStream_t stream) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, offsets, E, sch,
-                     skinny, fat, big);
-  return hipGetLastError();
-}
-
-
-static int cap_grid8(long long items, int cap) {
-  if (items < 1) items = 1;
-  return (int)(items < cap ? items : cap);
+template <bool GATEUP>
+__global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kG8Ring];
+  // the queue head is passed through the idle ring between items
+  int *next_item = reinterpret_cast<int *>(ring);
+  const uint32_t ring_lds = lds_addr(ring);
+  constexpr int FEAT = GATEUP ? 64 : 128;  // output features per item
+  const int per_tile = (a.N + FEAT - 1) / FEAT;
+  const int total = *a.ntiles * per_tile;
+  for (;;) {
+    if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
+    __syncthreads();
+    // read before g8_item's first barrier (its loads overwrite it)
+    const int it = __builtin_amdgcn_readfirstlane(*next_item);
+    if (it >= total) break;
+    const int ti = it / per_tile;
+    const int n0 = (it - ti * per_tile) * FEAT;
+    const Tile t = a.tiles[ti];
+    switch (t.ablk) {
+      case 8: g8_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
+      case 4: g8_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
+      case 2: g8_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
+      default: g8_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+    }
+    // the ring (and the queue head in it) is rewritten only after every wave
+    // has passed this barrier
+    __syncthreads();
+  }
 }
 
 hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream) {
   hipError_t err = hipSuccess;
   if (stages & kStagePlan) {
-    err = launch_schedule(L.offsets, L.E, L.sch, L.skinny, L.fat, nullptr, stream);
+    err = launch_grouped_schedule(L.offsets, L.E, L.sch, L.tiles, stream);
     if (err != hipSuccess) return err;
     err = launch_quant_rows(L.x, L.T, nullptr, L.d, L.qx, L.sx, L.grid_cap, stream);
     if (err != hipSuccess) return err;
   }
-  const long long max_skinny = L.E < L.R ? L.E : L.R;
-  const long long max_fat = L.R / kFatRows + L.E;  // no big class: fat tiles only
-
-  GemmArgs8 gu{};
-  gu.act = L.qx;
-  gu.act_scale = L.sx;
-  gu.sorted_routes = L.sorted_routes;
-  gu.k = L.k;
-  gu.w0 = L.wg;
-  gu.w1 = L.wu;
-  gu.s0 = L.sg;
-  gu.s1 = L.su;
-  gu.out = L.h;
-  gu.N = L.f;
-  gu.K = L.d;
-
+  Gg8Args g{};
+  g.k = L.k;
+  g.tiles = L.tiles;
+  g.ntiles = &L.sch->n_tiles;
   if (stages & kStageGateUp) {
-  gu.tiles = L.skinny;
-  gu.ntiles = &L.sch->n_skinny;
-  hipLaunchKernelGGL(skinny8_kernel<true>,
-                     dim3(cap_grid8(max_skinny * ((L.f + sk8_feat<true>() - 1) / sk8_feat<true>()),
-                                    L.grid_cap)),
-                     dim3(kSk8Threads), 0, stream, gu);
-  gu.tiles = L.fat;
-  gu.ntiles = &L.sch->n_fat;
-  hipLaunchKernelGGL(fat8_kernel<true>, dim3(cap_grid8(max_fat * (L.f / kFt8BN), L.grid_cap)),
-                     dim3(kFt8Threads), 0, stream, gu);
+    g.act = L.qx;
+    g.act_scale = L.sx;
+    g.sorted_routes = L.sorted_routes;
+    g.w0 = L.wg;
+    g.w1 = L.wu;
+    g.s0 = L.sg;
+    g.s1 = L.su;
+    g.out = L.h;
+    g.N = L.f;
+    g.K = L.d;
+    g.counter = &L.sch->counter[0];
+    hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
+                       g);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  if (!(stages & kStageDown)) return hipGetLastError();
-
-  // h -> per-row E4M3; the active row count is offsets[E]
-  err = launch_quant_rows(L.h, L.R, L.offsets + L.E, L.f, L.qh, L.sh, L.grid_cap, stream);
-  if (err != hipSuccess) return err;
-
-  GemmArgs8 dn{};
-  dn.act = L.qh;
-  dn.act_scale = L.sh;
-  dn.sorted_routes = nullptr;
-  dn.k = L.k;
-  dn.w0 = L.wd;
-  dn.w1 = nullptr;
-  dn.s0 = L.sd;
-  dn.s1 = nullptr;
-  dn.out = L.y;
-  dn.N = L.d;
-  dn.K = L.f;
-  dn.tiles = L.skinny;
-  dn.ntiles = &L.sch->n_skinny;
-  hipLaunchKernelGGL(skinny8_kernel<false>,
-                     dim3(cap_grid8(max_skinny * ((L.d + sk8_feat<false>() - 1) / sk8_feat<false>()),
-                                    L.grid_cap)),
-                     dim3(kSk8Threads), 0, stream, dn);
-  dn.tiles = L.fat;
-  dn.ntiles = &L.sch->n_fat;
-  hipLaunchKernelGGL(fat8_kernel<false>, dim3(cap_grid8(max_fat * (L.d / kFt8BN), L.grid_cap)),
-                     dim3(kFt8Threads), 0, stream, dn);
+  if (stages & kStageDown) {
+    // h -> per-row E4M3; the active row count is offsets[E]
+    err = launch_quant_rows(L.h, L.R, L.offsets + L.E, L.f, L.qh, L.sh, L.grid_cap, stream);
+    if (err != hipSuccess) return err;
+    g.act = L.qh;
+    g.act_scale = L.sh;
+    g.sorted_routes = nullptr;
+    g.w0 = L.wd;
+    g.w1 = nullptr;
+    g.s0 = L.sd;
+    g.s1 = nullptr;
+    g.out = L.y;
+    g.N = L.d;
+    g.K = L.f;
+    g.counter = &L.sch->counter[1];
+    hipLaunchKernelGGL(grouped_gemm8_kernel<false>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
+                       g);
+  }
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ struct GgArgs {
   const uint16_t *w1;  // up weights [E, N, K] (gate/up only)
   void *out;           // gate/up: h bf16 [R, N]; down: y fp32 [R, N]
   int N, K;
-  const Tile *tiles;   // tile.pad = ablk (row capacity / 32)
+  const Tile *tiles;
   const int *ntiles;
   int *counter;        // item queue head, zeroed by the schedule
 };
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     row0 = offsets[e];
     n = offsets[e + 1] - row0;
   }
-  const int nfull = n / kBigRows;
-  const int rem = n - nfull * kBigRows;
+  const int nfull = n / kTileRows;
+  const int rem = n - nfull * kTileRows;
   const int rab = rem == 0 ? 0 : rem <= 32 ? 1 : rem <= 64 ? 2 : rem <= 128 ? 4 : 8;
   int cnt[4] = {nfull + (rab == 8), rab == 4, rab == 2, rab == 1};  // ablk 8, 4, 2, 1
   int pos[4], tot[4];
@@ -102,24 +102,21 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
   for (int i = 0; i < cnt[0]; ++i) {
     Tile t;
     t.e = e;
-    t.row0 = row0 + i * kBigRows;
-    t.nrows = min(kBigRows, n - i * kBigRows);
-    t.pad = 8;
+    t.row0 = row0 + i * kTileRows;
+    t.nrows = min(kTileRows, n - i * kTileRows);
+    t.ablk = 8;
     tiles[pos[0] + i] = t;
   }
   if (rab > 0 && rab < 8) {
     const int c = rab == 4 ? 1 : rab == 2 ? 2 : 3;
     Tile t;
     t.e = e;
-    t.row0 = row0 + nfull * kBigRows;
+    t.row0 = row0 + nfull * kTileRows;
     t.nrows = rem;
-    t.pad = rab;
+    t.ablk = rab;
     tiles[pos[c]] = t;
   }
   if (e == 0) {
-    sch->n_big = tot[0];
-    sch->n_fat = tot[1] + tot[2];
-    sch->n_skinny = tot[3];
     sch->n_tiles = base;
     sch->counter[0] = 0;
     sch->counter[1] = 0;
@@ -298,12 +295,14 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   for (;;) {
     if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
     __syncthreads();
-    const int it = *next_item;  // read before gg_item's first barrier; its loads overwrite it
+    // read before gg_item's first barrier (its loads overwrite it); uniform,
+    // so the tile fetch below is a scalar load
+    const int it = __builtin_amdgcn_readfirstlane(*next_item);
     if (it >= total) break;
     const int ti = it / per_tile;
     const int n0 = (it - ti * per_tile) * FEAT;
     const Tile t = a.tiles[ti];
-    switch (t.pad) {
+    switch (t.ablk) {
       case 8: gg_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
       case 4: gg_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
       case 2: gg_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
@@ -317,16 +316,21 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
 
 // ------------------------------------------------------------------ host side
 
+hipError_t launch_grouped_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *tiles,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_schedule_kernel, dim3(1), dim3(kGsThreads), 0, stream, offsets, E,
+                     sch, tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream) {
   if (stages & kStagePlan) {
-    hipLaunchKernelGGL(grouped_schedule_kernel, dim3(1), dim3(kGsThreads), 0, stream, L.offsets,
-                       L.E, L.sch, L.big);
-    hipError_t err = hipGetLastError();
+    const hipError_t err = launch_grouped_schedule(L.offsets, L.E, L.sch, L.tiles, stream);
     if (err != hipSuccess) return err;
   }
   GgArgs g{};
   g.k = L.k;
-  g.tiles = L.big;
+  g.tiles = L.tiles;
   g.ntiles = &L.sch->n_tiles;
   if (stages & kStageGateUp) {
     g.act = L.x;

@@ -22,8 +22,10 @@ int quant_max_cols();
 hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream);
 
-hipError_t launch_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *skinny, Tile *fat,
-                           Tile *big, hipStream_t stream);
+// Tile list of the grouped FFN from the expert offsets (one thread per
+// expert); also zeroes the work-queue heads.
+hipError_t launch_grouped_schedule(const int32_t *offsets, int E, Schedule *sch, Tile *tiles,
+                                   hipStream_t stream);
 
 // Stages of the grouped FFN (bit mask).
 enum : int { kStagePlan = 1, kStageGateUp = 2, kStageDown = 4, kStageAll = 7 };
@@ -37,12 +39,9 @@ struct FfnLaunch {
   float *y;
   uint16_t *h;
   Schedule *sch;
-  Tile *skinny;
-  Tile *fat;
-  Tile *big;
+  Tile *tiles;
   int T, k, E, d, f, R;
-  int grid_cap;  // persistent workgroups per GEMM launch
-  int num_cus;
+  int num_cus;  // workgroups of each persistent GEMM launch
 };
 hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
 
@@ -61,11 +60,9 @@ struct FfnLaunchFp8 {
   uint8_t *qh;
   float *sh;
   Schedule *sch;
-  Tile *skinny;
-  Tile *fat;
-  Tile *big;
+  Tile *tiles;
   int T, k, E, d, f, R;
-  int grid_cap;
+  int grid_cap;  // workgroups of a row-quantisation launch
   int num_cus;
 };
 hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream);

@@ -5,9 +5,9 @@ Tolerances: bf16 max-abs <= 2e-2 and relative Frobenius <= 1e-3; fp8
 fp8) at the same point, so what is left is fp32 accumulation order and rare
 bf16 rounding-boundary flips of h.
 
-The per-expert row counts below put experts in every tile class: 1-16 rows
-(one 16-row skinny slab), 17-32 (two slabs), 33-128 (one fat tile), >128
-(full fat tiles plus a skinny or fat remainder), and empty experts.
+The per-expert row counts below put experts in every tile capacity and at
+its edges: remainders of 1-32 rows (32-row tiles), 33-64, 65-128 and
+129-256, full 256-row tiles plus a remainder, and empty experts.
 """
 import numpy as np
 import pytest
