@@ -225,8 +225,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(ach / pk, 4)}
     roof["traffic"] = traffic_from_profiles(name)
-    roof["kernel"] = ("grouped_gemm_kernel<true> (gate/up GEMM, SwiGLU epilogue)" if not fp8 else
-                      "gate/up stage (skinny8_kernel + fat8_kernel, SwiGLU epilogue)")
+    roof["kernel"] = ("grouped_gemm8_kernel<true>" if fp8 else "grouped_gemm_kernel<true>") + \
+        " (gate/up GEMM, SwiGLU epilogue)"
     roof["avg_ms"] = round(gu_avg, 5)
     roof["algorithmic_bytes"] = int(work["gate_up_bytes"])
     roof["algorithmic_flops"] = work["gate_up_flops"]
