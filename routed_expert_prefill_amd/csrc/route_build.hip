@@ -1,7 +1,8 @@
 // Route histogram, prefix and stable scatter for up to 256 experts
 // ("perf(ds4): batch heterogeneous MoE prefill by expert", Summary).
 //
-// Three launches over chunks of kChunk routes:
+// Up to 16384 routes: one workgroup does all three steps (rb_fused_kernel).
+// Beyond that, three launches over chunks of kChunk routes:
 //   1. per-chunk histogram in LDS (integer atomics: order-independent);
 //   2. one workgroup scans the chunk histograms per bin and the bin totals;
 //   3. per-chunk stable scatter: each wave walks its routes 64 at a time in
@@ -132,6 +133,85 @@ __global__ __launch_bounds__(kRbThreads) void rb_scatter_kernel(const int32_t *_
   }
 }
 
+// ------------------------------------------------------------------ small R
+
+// Up to kFusedMaxR routes: the same three steps in one workgroup, without the
+// two extra launches.  The histogram is one pass of LDS atomics; the scatter
+// walks the routes in order, 1024 at a time (64 per wave), and ranks each
+// lane among equal keys of its wave (ballots) and of the earlier waves
+// (per-wave counts in LDS) on top of the bin's running base.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxR = 16384;
+
+__global__ __launch_bounds__(kFusedThreads) void rb_fused_kernel(
+    const int32_t *__restrict__ ids, const uint8_t *__restrict__ mask, int R, int E, int key_bits,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_routes,
+    int32_t *__restrict__ route_rows) {
+  __shared__ int base[kMaxBins];  // histogram, then the running start of each bin
+  __shared__ int scan[kFusedThreads];
+  __shared__ int cnt[kFusedWaves][kMaxBins];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = lane_id();
+  if (tid <= E) base[tid] = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += kFusedThreads) atomicAdd(&base[route_key(ids, mask, r, E)], 1);
+  __syncthreads();
+  // exclusive prefix over the E + 1 bins (inclusive Hillis-Steele, shifted)
+  const int c = tid <= E ? base[tid] : 0;
+  scan[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < kFusedThreads; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = scan[tid] - c;
+  if (tid <= E) {
+    counts[tid] = c;
+    base[tid] = excl;
+  }
+  if (tid <= E + 1) offsets[tid] = excl;  // offsets[E + 1] = R
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r0 = 0; r0 < R; r0 += kFusedThreads) {
+    for (int i = tid; i < kFusedWaves * kMaxBins; i += kFusedThreads) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    const int r = r0 + tid;
+    const bool valid = r < R;
+    const int key = valid ? route_key(ids, mask, r, E) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < key_bits; ++bit) {
+      const bool set = (key >> bit) & 1;
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    if (valid && rank == 0) cnt[w][key] = __popcll(peers);
+    __syncthreads();
+    // per bin: the running start plus the counts of the earlier waves
+    if (tid <= E) {
+      int s = base[tid];
+      for (int v = 0; v < kFusedWaves; ++v) {
+        const int n = cnt[v][tid];
+        cnt[v][tid] = s;
+        s += n;
+      }
+      base[tid] = s;
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = cnt[w][key] + rank;
+      sorted_routes[pos] = r;
+      route_rows[r] = pos;
+    }
+    __syncthreads();
+  }
+}
+
 int route_chunks(int R) { return (R + kChunk - 1) / kChunk; }
 
 hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, int E,
@@ -142,6 +222,11 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
   int32_t *chunk_base = ws + (size_t)nchunks * (E + 1);
   int key_bits = 1;
   while ((1 << key_bits) < E + 1) ++key_bits;
+  if (R <= kFusedMaxR) {
+    hipLaunchKernelGGL(rb_fused_kernel, dim3(1), dim3(kFusedThreads), 0, stream, ids, mask, R, E,
+                       key_bits, counts, offsets, sorted_routes, route_rows);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(rb_hist_kernel, dim3(nchunks), dim3(kRbThreads), 0, stream, ids, mask, R, E,
                      chunk_hist);
   hipLaunchKernelGGL(rb_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nchunks,
