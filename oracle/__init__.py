@@ -25,6 +25,10 @@ What is computed, and where the pages state it:
   weighted by a dense gate matrix that is zero off the selected active routes.
 * ``moe.moe_ref_blocked`` -- the same fp64 mathematics, expert-major, with the
   products done by BLAS dgemm.  It is the timed CPU baseline.
+* ``router.route_topk`` -- top-k expert selection from router logits with
+  renormalised gates; the pages keep native top-6 routing and the selected-row
+  order ("perf(ds4): extend sparse prefill scheduling to 10K", Summary) and
+  leave the arithmetic to the model (reading in the module).
 * ``moe.combine_ref`` -- the fused route combine ("perf(ds4): accelerate ROCm
   decode and long-context selection", lucebox8 gfx1151 A/B; "... 10K",
   Historical fused-combine discriminator).

@@ -126,9 +126,9 @@ def _select_topk(z: np.ndarray, k: int):
     return order.astype(np.int32), gates
 
 
-def make_routing(wl: Workload, seed: int = 0) -> Routing:
-    rng = _main_rng(seed)
-    T, E, k, d = wl.T, wl.E, wl.k, wl.d
+def _draw_logits(rng, wl: Workload) -> np.ndarray:
+    """Router logits with the workload's expert bias added in fp32 (first draws)."""
+    T, E = wl.T, wl.E
     logits = rng.standard_normal((T, E), dtype=np.float32)
     if wl.routing == "bias":
         bias = (rng.standard_normal(E, dtype=np.float32) * np.float32(wl.bias_std)).astype(np.float32)
@@ -137,7 +137,18 @@ def make_routing(wl: Workload, seed: int = 0) -> Routing:
         bias = np.log(p / p.sum()).astype(np.float32)
     else:
         bias = np.zeros(E, dtype=np.float32)
-    z = (logits + bias[None, :]).astype(np.float32)
+    return (logits + bias[None, :]).astype(np.float32)
+
+
+def make_logits(wl: Workload, seed: int = 0) -> np.ndarray:
+    """fp32 [T, E]: the biased router logits make_routing selects from."""
+    return _draw_logits(_main_rng(seed), wl)
+
+
+def make_routing(wl: Workload, seed: int = 0) -> Routing:
+    rng = _main_rng(seed)
+    T, E, k, d = wl.T, wl.E, wl.k, wl.d
+    z = _draw_logits(rng, wl)
     ids, gates = _select_topk(z, k)
     u = rng.random((T, k))
     mask = (u >= wl.mask_p).astype(np.uint8)
