@@ -233,6 +233,24 @@ def main():
     t_path_roof = max(work["path_bytes"] / (HBM_PEAK_GBS * 1e9),
                       work["path_flops"] / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12))
 
+    # the router ahead of the path (moe_route_topk), timed on its own: it is
+    # not part of the step, whose routing is an input
+    logits = torch.from_numpy(synth.make_logits(wl, seed=0)).to(dev)
+    for _ in range(3):
+        rep.route_topk(logits, wl.k)
+    rev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    n_router = 20
+    rev[0].record(stream)
+    for _ in range(n_router):
+        rep.route_topk(logits, wl.k)
+    rev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    router_ms = rev[0].elapsed_time(rev[1]) / n_router
+    router_bytes = wl.T * wl.E * 4 + wl.T * wl.k * 8
+    router = {"call": "moe_route_topk", "ms": round(router_ms, 5),
+              "gb_s": round(router_bytes / (router_ms / 1e3) / 1e9, 1),
+              "algorithmic_bytes": router_bytes}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -262,6 +280,7 @@ def main():
                  "active_rows": work["R_act"], "experts_used": work["experts_used"],
                  "stage_bytes": work["stage_bytes"]},
         "roofline": roof,
+        "router": router,
         "cpu_baseline": cpu,
         "kernel_source_sha": source_hash(),
     }

@@ -4,6 +4,8 @@
  * The library computes one routed-expert MoE layer for a prefill chunk of T
  * tokens, each routed to k of E experts, in expert-major order:
  *
+ *   moe_route_topk    (optional, ahead of the path) top-k experts and
+ *                     renormalised gates from router logits;
  *   moe_route_build   route histogram, prefix and scatter into
  *                     expert-contiguous order ("perf(ds4): batch heterogeneous
  *                     MoE prefill by expert", Summary: GPU-native route
@@ -202,6 +204,26 @@ int moe_ffn_down(const moe_ffn_desc *desc /* host */, const int32_t *offsets, co
 int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
                 const uint8_t *route_mask, int T, int k, int d, float *out,
                 moe_stream_t stream);
+
+/* ------------------------------------------------------------ router
+ * Top-k expert selection and gates from router logits, the step ahead of
+ * moe_route_build.  The pages keep the model's native top-6 routing and its
+ * selected-row order ("perf(ds4): extend sparse prefill scheduling to 10K",
+ * Summary); the arithmetic is the usual renormalised-softmax router:
+ *
+ *   z[t,e]      = logits[t,e] + bias[e]        (one fp32 addition; z = logits if bias is NULL)
+ *   topk_ids[t] = the k largest z[t,.], descending; equal z go to the lower expert index
+ *   topk_w[t,j] = exp(z_j - z_max) / sum_i exp(z_i - z_max), i over the selected experts,
+ *                 evaluated in fp64 (sum in ascending j) and rounded once to fp32
+ *
+ * logits fp32 [T,E] row-major, finite; bias fp32 [E] or NULL;
+ * topk_ids int32 [T,k] and topk_w fp32 [T,k] are written in full.
+ * Errors: MOE_EINVAL (null logits or outputs, T < 1, E < 1, k < 1, T*E
+ *         overflows int), MOE_EUNSUPPORTED (E > 256, k > 16 or k > E),
+ *         MOE_EALIGN, MOE_EHIP.
+ */
+int moe_route_topk(const float *logits, const float *bias, int T, int E, int k,
+                   int32_t *topk_ids, float *topk_w, moe_stream_t stream);
 
 /* ------------------------------------------------------------ fp8 row quantisation
  * The activation quantisation the fp8 mode applies to x (exposed so callers

@@ -16,7 +16,7 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_E4M3_ROW, MOE_W_BF16, MOE_W_FP8_E4M
                    LibraryNotBuilt, MoeFfnDesc)
 
 __all__ = [
-    "route_build", "grouped_ffn", "combine", "quant_rows_fp8", "MoEPrefill", "RouteTable",
+    "route_topk", "route_build", "grouped_ffn", "combine", "quant_rows_fp8", "MoEPrefill", "RouteTable",
     "ffn_desc", "ffn_plan", "ffn_gate_up", "ffn_down", "LibraryNotBuilt", "load_library",
 ]
 
@@ -59,6 +59,29 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def route_topk(logits, k: int, bias=None, topk_ids=None, topk_w=None):
+    """moe_route_topk: top-k experts (descending, ties to the lower index) and
+    renormalised gates from fp32 router logits [T, E]."""
+    torch = _torch()
+    lib = _lib.load()
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+        if bias.numel() != E:
+            raise ValueError("bias must have E entries")
+    if topk_ids is None:
+        topk_ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    rc = lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, _ptr(topk_ids), _ptr(topk_w),
+                            _stream())
+    _lib.check(rc, "moe_route_topk")
+    return topk_ids, topk_w
 
 
 def route_build(topk_ids, route_mask, E: int, out: Optional[RouteTable] = None,

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_prefill.so")
 
-HIP_SOURCES = ["route_build.hip", "combine.hip", "quant.hip", "ffn_grouped.hip", "ffn_fp8.hip"]
+HIP_SOURCES = ["route_topk.hip", "route_build.hip", "combine.hip", "quant.hip", "ffn_grouped.hip",
+               "ffn_fp8.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

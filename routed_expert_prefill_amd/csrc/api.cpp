@@ -269,6 +269,18 @@ int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int moe_route_topk(const float *logits, const float *bias, int T, int E, int k,
+                   int32_t *topk_ids, float *topk_w, moe_stream_t stream) {
+  if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (T < 1 || E < 1 || k < 1 || (long long)T * E >= (1LL << 31)) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_EUNSUPPORTED;
+  if (misaligned(logits) || misaligned(topk_ids) || misaligned(topk_w) || (bias && misaligned(bias)))
+    return MOE_EALIGN;
+  return status_from(moe::launch_route_topk(logits, bias, T, E, k, topk_ids, topk_w,
+                                            num_cus_current_device() * 8,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int moe_quant_rows_fp8(const void *x, int rows, int cols, uint8_t *q, float *s,
                        moe_stream_t stream) {
   if (!x || !q || !s || rows < 1 || cols < 1) return MOE_EINVAL;

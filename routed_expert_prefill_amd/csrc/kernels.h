@@ -18,6 +18,9 @@ hipError_t launch_combine(const float *y, const int32_t *route_rows, const float
                           const uint8_t *mask, int T, int k, int d, float *out,
                           hipStream_t stream);
 
+hipError_t launch_route_topk(const float *logits, const float *bias, int T, int E, int k,
+                             int32_t *ids, float *gates, int grid_cap, hipStream_t stream);
+
 int quant_max_cols();
 hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream);

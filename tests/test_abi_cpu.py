@@ -146,6 +146,24 @@ def test_quant_errors(lib):
     assert qf(q=A + 8) == _lib.MOE_EALIGN
 
 
+def test_route_topk_errors(lib):
+    r = lambda lg=A, b=0, T=4, E=16, k=6, ids=A, w=A: lib.moe_route_topk(  # noqa: E731
+        lg, b or None, T, E, k, ids, w, None)
+    assert r(lg=0) == _lib.MOE_EINVAL
+    assert r(ids=0) == _lib.MOE_EINVAL
+    assert r(w=0) == _lib.MOE_EINVAL
+    assert r(T=0) == _lib.MOE_EINVAL
+    assert r(E=0) == _lib.MOE_EINVAL
+    assert r(k=0) == _lib.MOE_EINVAL
+    assert r(T=1 << 24, E=256) == _lib.MOE_EINVAL  # T*E overflows int
+    assert r(E=257) == _lib.MOE_EUNSUPPORTED
+    assert r(k=17, E=64) == _lib.MOE_EUNSUPPORTED
+    assert r(k=9, E=8) == _lib.MOE_EUNSUPPORTED
+    assert r(lg=A + 4) == _lib.MOE_EALIGN
+    assert r(b=A + 4) == _lib.MOE_EALIGN
+    assert r(w=A + 8) == _lib.MOE_EALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

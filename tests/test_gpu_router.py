@@ -1,0 +1,68 @@
+"""GPU router (moe_route_topk) vs the fp64 oracle: ids bit-exact, gates within
+one fp32 ulp (both sides evaluate the gates in fp64 and round once; only the
+exp implementations differ, in the last bits of the double)."""
+import numpy as np
+import pytest
+
+from oracle.router import route_topk as route_topk_ref
+from routed_expert_prefill_amd import synth
+from gpu_util import np_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(logits, k, bias=None):
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    ids, w = rep.route_topk(np_dev(logits), k, None if bias is None else np_dev(bias))
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _check(logits, k, bias=None):
+    gi, gw = _gpu(logits, k, bias)
+    ri, rw = route_topk_ref(logits, bias, k)
+    assert np.array_equal(gi, ri)
+    assert np.all(np.abs(gw - rw) <= np.spacing(rw)), np.abs(gw - rw).max()
+    return gi, gw
+
+
+@pytest.mark.parametrize("T,E,k,seed", [
+    (1, 1, 1, 0), (5, 7, 7, 1), (33, 64, 6, 2), (100, 256, 6, 3), (17, 256, 16, 4),
+    (64, 100, 3, 5), (257, 255, 8, 6),
+])
+def test_random_logits(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    _check(rng.standard_normal((T, E)).astype(np.float32), k)
+
+
+def test_ties_and_bias():
+    rng = np.random.default_rng(7)
+    lg = rng.integers(-2, 3, (200, 256)).astype(np.float32)  # heavy ties
+    _check(lg, 6)
+    _check(lg, 16)
+    bias = (rng.standard_normal(256) * 0.5).astype(np.float32)
+    _check(rng.standard_normal((300, 256)).astype(np.float32), 6, bias)
+    one = np.float32(1.0)
+    up = np.nextafter(one, np.float32(2))
+    gi, gw = _check(np.array([[one, up]], np.float32), 2, np.array([0.6 * 2.0 ** -23, 0.0], np.float32))
+    assert gi.tolist() == [[0, 1]]
+    _check(np.full((4, 32), -3.5, np.float32), 5)  # all equal
+    lg2 = rng.standard_normal((8, 40)).astype(np.float32)
+    lg2[:, 10:] = -np.inf  # -inf logits are never selected while k finite ones remain
+    _check(lg2, 6)
+
+
+@pytest.mark.parametrize("name", ["prefill_T401_uniform_bf16", "prefill_T2048_biased_bf16",
+                                  "prefill_T8192_zipf_bf16"])
+def test_workload_logits_match_generator(name):
+    wl = synth.WORKLOADS[name]
+    z = synth.make_logits(wl, seed=0)
+    r = synth.make_routing(wl, seed=0)
+    gi, gw = _gpu(z, wl.k)
+    assert np.array_equal(gi, r.topk_ids)
+    assert np.all(np.abs(gw - r.topk_w) <= np.spacing(r.topk_w))
+    if wl.T <= 2048:
+        _check(z, wl.k)
