@@ -13,6 +13,7 @@ inside the timed region) and the CPU oracle's throughput on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -144,6 +145,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time spent on the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--owner", default=None, metavar="G:g",
+                    help="measure one owner's share: experts split into G contiguous ranges, "
+                         "only routes to range g stay active (the sharded layout on one GPU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 1 GiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -174,6 +178,14 @@ def main():
     t0 = time.perf_counter()
     r, ten = synth.device_inputs(wl, seed=0, device=dev)
     log(f"inputs for {name} generated and resident in HBM in {time.perf_counter() - t0:.1f} s")
+
+    owner = None
+    if args.owner:
+        G, g = (int(v) for v in args.owner.split(":"))
+        r = dataclasses.replace(r, route_mask=synth.owner_mask(r.topk_ids, r.route_mask, wl.E, G, g))
+        ten["route_mask"] = torch.from_numpy(r.route_mask).to(dev)
+        owner = f"{g} of {G}"
+        log(f"owner {owner}: {int(r.route_mask.sum())} of {r.route_mask.size} routes active")
 
     run = rep.MoEPrefill(wl.T, wl.k, wl.E, wl.d, wl.f, fp8=fp8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -272,7 +284,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
                    "routing": wl.routing, "mask_p": wl.mask_p, "weights": wl.dtype,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu" if owner is None else f"expert owner {owner}"},
         "path": {"tflops": round(work["path_flops"] / (ms_step / 1e3) / 1e12, 2),
                  "algorithmic_gb": round(work["path_bytes"] / 1e9, 3),
                  "hbm_gbs": round(work["path_bytes"] / (ms_step / 1e3) / 1e9, 1),

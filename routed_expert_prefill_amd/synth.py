@@ -145,6 +145,17 @@ def make_logits(wl: Workload, seed: int = 0) -> np.ndarray:
     return _draw_logits(_main_rng(seed), wl)
 
 
+def owner_mask(topk_ids: np.ndarray, route_mask: np.ndarray, E: int, G: int, g: int) -> np.ndarray:
+    """Route mask of owner g of G when experts are split into G contiguous
+    ranges of E/G: a route stays active only if its expert lies in
+    [g*E/G, (g+1)*E/G).  Other owners' routes fall into the masked bin."""
+    if E % G or not 0 <= g < G:
+        raise ValueError("need G | E and 0 <= g < G")
+    lo, hi = g * (E // G), (g + 1) * (E // G)
+    own = (topk_ids >= lo) & (topk_ids < hi)
+    return (route_mask.astype(bool) & own).astype(np.uint8)
+
+
 def make_routing(wl: Workload, seed: int = 0) -> Routing:
     rng = _main_rng(seed)
     T, E, k, d = wl.T, wl.E, wl.k, wl.d
@@ -230,7 +241,8 @@ def approx_host_bytes(wl: Workload) -> int:
 
 
 __all__ = [
-    "Workload", "WORKLOADS", "DEFAULT_BENCH_WORKLOAD", "Routing", "make_routing",
+    "Workload", "WORKLOADS", "DEFAULT_BENCH_WORKLOAD", "Routing", "make_routing", "make_logits",
+    "owner_mask",
     "expert_weights", "all_expert_weights", "SCALE_BLOCK", "weight_bytes_per_expert",
     "approx_host_bytes", "f32_to_bf16_bits", "f32_to_e4m3_codes",
 ]
