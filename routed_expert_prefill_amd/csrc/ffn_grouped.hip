@@ -41,6 +41,7 @@ struct GgArgs {
   const Tile *tiles;
   const int *ntiles;
   int *counter;        // item queue head, zeroed by the schedule
+  int wr;              // weight rows per item: 256, or 128 / 64 when every tile holds <= 32 rows
 };
 
 constexpr int kGgThreads = 512;
@@ -50,10 +51,10 @@ constexpr int kGgRing = 160 * 1024;  // the whole LDS of a workgroup
 
 // Ring geometry of an item with 32 * AB activation rows: a stage is
 // (32 AB + 256) rows of 128 bytes, and the ring has as many slots as fit.
-template <int AB>
+template <int AB, int WR = kGgWRows>
 struct GgRing {
-  static constexpr int kSlot = (32 * AB + kGgWRows) * 128;
-  static constexpr int kDepth = kGgRing / kSlot;
+  static constexpr int kSlot = (32 * AB + WR) * 128;
+  static constexpr int kDepth = (kGgRing / kSlot) < 12 ? (kGgRing / kSlot) : 12;
 };
 
 // ------------------------------------------------------------------ schedule
@@ -146,23 +147,26 @@ __device__ __forceinline__ f32x4 quad(const f32x16 &v, int g) {
 
 // Operand tiles a wave multiplies for one stage: TT activation tiles and TW
 // weight tiles of 32 rows, for the four 16-wide reduction steps.
-template <int AB>
+// With fewer weight rows per item (WR < 256, 32-row tiles only) waves
+// WR/32 .. 7 only load.
+template <int AB, int WR = kGgWRows>
 struct GgLayout {
   static constexpr int TT = AB == 8 ? 4 : AB;
   static constexpr int TW = AB == 8 ? 2 : 1;
+  __device__ static bool active(int wv) { return WR == kGgWRows || wv < WR / 32; }
   // LDS row (within the stage) of activation tile tt / weight tile tw of wave wv
   __device__ static int arow(int wv, int tt) { return AB == 8 ? ((wv >> 2) * 128 + tt * 32) : tt * 32; }
   __device__ static int wtile(int wv, int tw) { return AB == 8 ? ((wv & 3) * 2 + tw) : wv; }
   __device__ static int wrow(int wv, int tw) { return 32 * AB + 32 * wtile(wv, tw); }
 };
 
-template <bool GATEUP, int AB>
+template <bool GATEUP, int AB, int WR = kGgWRows>
 __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
                                         uint32_t ring_lds) {
-  using L = GgLayout<AB>;
+  using L = GgLayout<AB, WR>;
   constexpr int TT = L::TT, TW = L::TW;
-  constexpr int NA = 4 * AB;    // activation loads (8 rows each) per stage
-  constexpr int NL = NA + 32;   // all loads per stage
+  constexpr int NA = 4 * AB;       // activation loads (8 rows each) per stage
+  constexpr int NL = NA + WR / 8;  // all loads per stage
   constexpr int MAXJ = (NL + kGgWaves - 1) / kGgWaves;
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -198,8 +202,8 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
       src[j] = w + ((size_t)t.e * a.N + n) * K + lq * 8;
     }
   }
-  constexpr int NS = GgRing<AB>::kDepth;
-  constexpr int SLOT = GgRing<AB>::kSlot;
+  constexpr int NS = GgRing<AB, WR>::kDepth;
+  constexpr int SLOT = GgRing<AB, WR>::kSlot;
   auto issue = [&](int s, int slot) {
     const uint32_t base = ring_lds + (uint32_t)(slot * SLOT);
 #pragma unroll
@@ -239,6 +243,7 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
     const uint8_t *buf = ring + slot * SLOT;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (!L::active(wv)) break;
       bf16x8 fa[TT], fw[TW];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
@@ -255,6 +260,7 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
   }
 
   // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
+  if (!L::active(wv)) return;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int row = L::arow(wv, tt) + rr;
@@ -289,7 +295,9 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   // the queue head is passed through the idle ring between items
   int *next_item = reinterpret_cast<int *>(ring);
   const uint32_t ring_lds = lds_addr(ring);
-  constexpr int FEAT = GATEUP ? 128 : 256;  // output features per item
+  // output features per item: half the weight rows for gate/up (gate and up
+  // rows of the same features), all of them for down
+  const int FEAT = GATEUP ? a.wr / 2 : a.wr;
   const int per_tile = (a.N + FEAT - 1) / FEAT;
   const int total = *a.ntiles * per_tile;
   for (;;) {
@@ -302,11 +310,17 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
     const int ti = it / per_tile;
     const int n0 = (it - ti * per_tile) * FEAT;
     const Tile t = a.tiles[ti];
-    switch (t.ablk) {
-      case 8: gg_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
-      case 4: gg_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
-      case 2: gg_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
-      default: gg_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+    if (a.wr == 128) {
+      gg_item<GATEUP, 1, 128>(a, t, n0, ring, ring_lds);
+    } else if (a.wr == 64) {
+      gg_item<GATEUP, 1, 64>(a, t, n0, ring, ring_lds);
+    } else {
+      switch (t.ablk) {
+        case 8: gg_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
+        case 4: gg_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
+        case 2: gg_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
+        default: gg_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+      }
     }
     // the ring (and the queue head in it) is rewritten only after every wave
     // has passed this barrier
@@ -321,6 +335,32 @@ hipError_t launch_grouped_schedule(const int32_t *offsets, int E, Schedule *sch,
   hipLaunchKernelGGL(grouped_schedule_kernel, dim3(1), dim3(kGsThreads), 0, stream, offsets, E,
                      sch, tiles);
   return hipGetLastError();
+}
+
+// Weight rows per item.  With at most 32 routed rows in all (decode-sized
+// chunks) every tile is a 32-row tile and items may be narrowed to 128 or 64
+// weight rows: the weight stream then spreads over more CUs.  The choice
+// minimises (rounds of items over the CUs) x (weight rows per item + 32),
+// counting at most min(R, E) tiles; the 32 rows stand for an item's fixed
+// cost (ring fill and queue round trip, ~4 us, measured) and ties go to the
+// wider item.  n_out: output features of the projection; mats: weight
+// matrices interleaved in an item (2 for gate/up).
+static int item_weight_rows(const FfnLaunch &L, int n_out, int mats) {
+  if (L.R > 32) return kGgWRows;
+  const long long tiles = L.R < L.E ? L.R : L.E;
+  const int cus = L.num_cus > 0 ? L.num_cus : 1;
+  int best = kGgWRows;
+  long long best_cost = -1;
+  for (int wr = kGgWRows; wr >= 64; wr /= 2) {
+    const long long per_tile = (n_out + wr / mats - 1) / (wr / mats);
+    const long long rounds = (tiles * per_tile + cus - 1) / cus;
+    const long long cost = rounds * (wr + 32);
+    if (best_cost < 0 || cost < best_cost) {
+      best = wr;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream) {
@@ -341,6 +381,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.N = L.f;
     g.K = L.d;
     g.counter = &L.sch->counter[0];
+    g.wr = item_weight_rows(L, L.f, 2);
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(L.num_cus), dim3(kGgThreads), 0, stream, g);
   }
   if (stages & kStageDown) {
@@ -352,6 +393,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.N = L.d;
     g.K = L.f;
     g.counter = &L.sch->counter[1];
+    g.wr = item_weight_rows(L, L.d, 1);
     hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(L.num_cus), dim3(kGgThreads), 0, stream,
                        g);
   }

@@ -127,6 +127,28 @@ def test_tiny_workload_random_routing(fp8):
     assert np.all(out[3] == 0) and not np.any(np.signbit(out[3]))
 
 
+@pytest.mark.parametrize("T,d,f,seed", [(1, 256, 384, 20), (3, 384, 256, 21), (4, 512, 2048, 22),
+                                         (5, 256, 256, 23)])
+def test_decode_sized_chunks(T, d, f, seed):
+    """At most 32 routed rows: items narrowed to 128 or 64 weight rows (4, 512,
+    2048 takes 128 for gate/up and 64 for down on a 256-CU device)."""
+    rng = np.random.default_rng(seed)
+    k, E = 6, 64
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if T >= 3:
+        ids[1] = ids[0]  # an expert with more than one row
+    mask = (rng.random((T, k)) >= 0.2).astype(np.uint8)
+    w = rng.random((T, k)).astype(np.float32)
+    x = _x(T, d, seed + 1)
+    W = _weights(E, d, f, False, seed + 2)
+    run, out = _run(ids, w, mask, x, W, E, False, y_fill=float("nan"))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E)
+    _check(out, ref, BF16_TOL)
+    n_act = int(run.rt.offsets[E].item())
+    y = run.y.cpu().numpy()
+    assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
+
+
 def test_single_expert_single_route_is_dense_mlp():
     """E = 1, k = 1, gate 1, no mask: a dense SwiGLU MLP, checked also against
     torch's own matmul on the GPU (an independent library product)."""
