@@ -205,6 +205,25 @@ int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
                 const uint8_t *route_mask, int T, int k, int d, float *out,
                 moe_stream_t stream);
 
+/* ------------------------------------------------------------ combine, shared-output form
+ * The combine writing into the layer's shared-expert output (the fused
+ * combine's "shared-output" cases, "perf(ds4): extend sparse prefill
+ * scheduling to 10K", Historical fused-combine discriminator):
+ *
+ *   routed[t]   = the moe_combine sum (fp32, ascending j from +0.0, masked routes never read)
+ *   out[t]      = routed[t] + shared[t]   (one fp32 addition; out = routed if shared is NULL)
+ *   out_bf16[t] = bf16 round-to-nearest-even of out[t]
+ *
+ * shared fp32 [T,d] or NULL; out fp32 [T,d] or NULL; out_bf16 bf16 [T,d] or
+ * NULL (at least one of out, out_bf16).  Other arguments as for moe_combine.
+ * Errors: MOE_EINVAL (null y/route_rows/topk_w, both outputs null, T < 1,
+ *         k < 1, d < 4 or d not a multiple of 4), MOE_EUNSUPPORTED (k > 16),
+ *         MOE_EALIGN, MOE_EHIP.
+ */
+int moe_combine_shared(const float *y, const int32_t *route_rows, const float *topk_w,
+                       const uint8_t *route_mask, const float *shared, int T, int k, int d,
+                       float *out, void *out_bf16, moe_stream_t stream);
+
 /* ------------------------------------------------------------ router
  * Top-k expert selection and gates from router logits, the step ahead of
  * moe_route_build.  The pages keep the model's native top-6 routing and its

@@ -171,6 +171,25 @@ def combine_ref(y: np.ndarray, route_rows: np.ndarray, topk_w: np.ndarray,
     return out
 
 
+def combine_shared_ref(y: np.ndarray, route_rows: np.ndarray, topk_w: np.ndarray,
+                       route_mask: Optional[np.ndarray], shared: Optional[np.ndarray], T: int,
+                       k: int) -> np.ndarray:
+    """The combine writing into a shared-expert output (fp64).
+
+    The fused combine's "shared-output" cases ("perf(ds4): extend sparse
+    prefill scheduling to 10K", Historical fused-combine discriminator) add
+    the routed sum to the output of the layer's shared expert.  Reading: the
+    routed sum is formed exactly as in ``combine_ref`` and the shared row is
+    added once at the end, out[t] = routed[t] + shared[t]; with no shared
+    output it is the routed sum.  A bf16 copy of out, when asked for, is its
+    round-to-nearest-even (``numerics.bf16_round``).
+    """
+    out = combine_ref(y, route_rows, topk_w, route_mask, T, k)
+    if shared is not None:
+        out = out + np.asarray(shared, dtype=np.float64)
+    return out
+
+
 def moe_ref_blocked(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
                     route_mask: Optional[np.ndarray], experts: ExpertSource, E: int,
                     fp8: bool = False, expert_subset: Optional[Iterable[int]] = None):

@@ -16,7 +16,7 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_E4M3_ROW, MOE_W_BF16, MOE_W_FP8_E4M
                    LibraryNotBuilt, MoeFfnDesc)
 
 __all__ = [
-    "route_topk", "route_build", "grouped_ffn", "combine", "quant_rows_fp8", "MoEPrefill", "RouteTable",
+    "route_topk", "route_build", "grouped_ffn", "combine", "combine_shared", "quant_rows_fp8", "MoEPrefill", "RouteTable",
     "ffn_desc", "ffn_plan", "ffn_gate_up", "ffn_down", "LibraryNotBuilt", "load_library",
 ]
 
@@ -203,6 +203,37 @@ def combine(y, route_rows, topk_w, route_mask, out=None):
                          _ptr(out), _stream())
     _lib.check(rc, "moe_combine")
     return out
+
+
+def combine_shared(y, route_rows, topk_w, route_mask, shared=None, out=None, out_bf16=None,
+                   want_fp32=True, want_bf16=False):
+    """moe_combine_shared: routed combine plus the shared-expert rows, as fp32
+    and/or bf16 (round to nearest even)."""
+    torch = _torch()
+    lib = _lib.load()
+    _need(y, "y", torch.float32, 2)
+    _need(route_rows, "route_rows", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    if route_mask is not None:
+        _need(route_mask, "route_mask", torch.uint8, 2)
+    T, k = topk_w.shape
+    d = y.shape[1]
+    if shared is not None:
+        _need(shared, "shared", torch.float32, 2)
+        if tuple(shared.shape) != (T, d):
+            raise ValueError("shared must be [T, d]")
+    if out is None and want_fp32:
+        out = torch.empty(T, d, dtype=torch.float32, device=y.device)
+    if out_bf16 is None and want_bf16:
+        out_bf16 = torch.empty(T, d, dtype=torch.bfloat16, device=y.device)
+    if out is not None:
+        _need(out, "out", torch.float32, 2)
+    if out_bf16 is not None:
+        _need(out_bf16, "out_bf16", torch.bfloat16, 2)
+    rc = lib.moe_combine_shared(_ptr(y), _ptr(route_rows), _ptr(topk_w), _ptr(route_mask),
+                                _ptr(shared), T, k, d, _ptr(out), _ptr(out_bf16), _stream())
+    _lib.check(rc, "moe_combine_shared")
+    return out, out_bf16
 
 
 def quant_rows_fp8(x, q=None, s=None):

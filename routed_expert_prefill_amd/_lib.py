@@ -23,7 +23,7 @@ EXPORTED = [
     "moe_route_build_workspace", "moe_route_build",
     "moe_grouped_ffn_workspace", "moe_grouped_ffn",
     "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
-    "moe_combine", "moe_quant_rows_fp8", "moe_route_topk",
+    "moe_combine", "moe_quant_rows_fp8", "moe_route_topk", "moe_combine_shared",
 ]
 
 
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_quant_rows_fp8.restype = i32
     lib.moe_quant_rows_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.moe_combine_shared.restype = i32
+    lib.moe_combine_shared.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.moe_route_topk.restype = i32
     lib.moe_route_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     _lib = lib

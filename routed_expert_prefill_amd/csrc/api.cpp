@@ -265,7 +265,21 @@ int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
   if (misaligned(y) || misaligned(route_rows) || misaligned(topk_w) || misaligned(out) ||
       (route_mask && misaligned(route_mask)))
     return MOE_EALIGN;
-  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, T, k, d, out,
+  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, nullptr, T, k, d, out,
+                                         nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine_shared(const float *y, const int32_t *route_rows, const float *topk_w,
+                       const uint8_t *route_mask, const float *shared, int T, int k, int d,
+                       float *out, void *out_bf16, moe_stream_t stream) {
+  if (!y || !route_rows || !topk_w || (!out && !out_bf16)) return MOE_EINVAL;
+  if (T < 1 || k < 1 || d < 4 || d % 4 != 0 || (long long)T * k >= (1LL << 31)) return MOE_EINVAL;
+  if (k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+  const void *ptrs[] = {y, route_rows, topk_w, route_mask, shared, out, out_bf16};
+  for (const void *p : ptrs)
+    if (p && misaligned(p)) return MOE_EALIGN;
+  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, shared, T, k, d, out,
+                                         static_cast<uint16_t *>(out_bf16),
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -4,6 +4,11 @@
 // consecutive fp32 columns and sums its token's active routes in ascending
 // route order from +0.0.  Masked routes are skipped by a branch, never
 // multiplied by zero, so nothing they hold can reach the output.
+//
+// Shared-output form ("perf(ds4): extend sparse prefill scheduling to 10K",
+// Historical fused-combine discriminator): the row of the shared expert's
+// output is added once to the routed sum, and a bf16 copy (round to nearest
+// even) can be written beside or instead of the fp32 row.
 #include "kernels.h"
 
 namespace moe {
@@ -14,8 +19,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float *__re
                                                                const int32_t *__restrict__ route_rows,
                                                                const float *__restrict__ topk_w,
                                                                const uint8_t *__restrict__ mask,
+                                                               const float *__restrict__ shared,
                                                                int T, int k, int d, int slices,
-                                                               float *__restrict__ out) {
+                                                               float *__restrict__ out,
+                                                               uint16_t *__restrict__ out_bf16) {
   const int t = blockIdx.x / slices;
   const int c = ((blockIdx.x - t * slices) * kCombThreads + threadIdx.x) * 4;
   if (c >= d) return;
@@ -30,16 +37,30 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float *__re
     acc[2] = __builtin_fmaf(w, v[2], acc[2]);
     acc[3] = __builtin_fmaf(w, v[3], acc[3]);
   }
-  *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = acc;
+  const size_t o = (size_t)t * d + c;
+  if (shared != nullptr) {
+    const f32x4 sh = *reinterpret_cast<const f32x4 *>(shared + o);
+    acc[0] += sh[0];
+    acc[1] += sh[1];
+    acc[2] += sh[2];
+    acc[3] += sh[3];
+  }
+  if (out != nullptr) *reinterpret_cast<f32x4 *>(out + o) = acc;
+  if (out_bf16 != nullptr) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+    v.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+    *reinterpret_cast<uint2 *>(out_bf16 + o) = v;
+  }
 }
 
 hipError_t launch_combine(const float *y, const int32_t *route_rows, const float *topk_w,
-                          const uint8_t *mask, int T, int k, int d, float *out,
-                          hipStream_t stream) {
+                          const uint8_t *mask, const float *shared, int T, int k, int d,
+                          float *out, uint16_t *out_bf16, hipStream_t stream) {
   const int per_block = kCombThreads * 4;
   const int slices = (d + per_block - 1) / per_block;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T * slices), dim3(kCombThreads), 0, stream, y,
-                     route_rows, topk_w, mask, T, k, d, slices, out);
+                     route_rows, topk_w, mask, shared, T, k, d, slices, out, out_bf16);
   return hipGetLastError();
 }
 

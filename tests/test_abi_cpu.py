@@ -137,6 +137,18 @@ def test_combine_errors(lib):
     assert c(m=A + 3) == _lib.MOE_EALIGN
 
 
+def test_combine_shared_errors(lib):
+    c = lambda y=A, rr=A, w=A, m=0, sh=0, T=4, k=2, d=64, out=A, ob=0: lib.moe_combine_shared(  # noqa: E731
+        y, rr, w, m or None, sh or None, T, k, d, out or None, ob or None, None)
+    assert c(y=0) == _lib.MOE_EINVAL
+    assert c(out=0, ob=0) == _lib.MOE_EINVAL  # no output at all
+    assert c(T=0) == _lib.MOE_EINVAL
+    assert c(d=6) == _lib.MOE_EINVAL
+    assert c(k=17) == _lib.MOE_EUNSUPPORTED
+    assert c(sh=A + 4) == _lib.MOE_EALIGN
+    assert c(out=0, ob=A + 2) == _lib.MOE_EALIGN
+
+
 def test_quant_errors(lib):
     qf = lambda x=A, rows=4, cols=256, q=A, s=A: lib.moe_quant_rows_fp8(x, rows, cols, q, s, None)  # noqa: E731
     assert qf(x=0) == _lib.MOE_EINVAL

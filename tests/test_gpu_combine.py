@@ -71,3 +71,44 @@ def test_no_mask_means_all_active():
     y, rr, w, _ = _case(7, 10, 3, 32, 0.0)
     ones = np.ones((10, 3), np.uint8)
     assert np.array_equal(_run(y, rr, w, None), _run(y, rr, w, ones))
+
+
+def _run_shared(y, rr, w, mask, shared, want_fp32=True, want_bf16=True):
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    out, ob = rep.combine_shared(np_dev(y), np_dev(rr), np_dev(w),
+                                 None if mask is None else np_dev(mask),
+                                 None if shared is None else np_dev(shared),
+                                 want_fp32=want_fp32, want_bf16=want_bf16)
+    torch.cuda.synchronize()
+    o = None if out is None else out.cpu().numpy()
+    b = None if ob is None else ob.view(torch.int16).cpu().numpy().view(np.uint16)
+    return o, b
+
+
+@pytest.mark.parametrize("seed,T,k,d,p", [(10, 401, 6, 4096, 0.05), (11, 7, 16, 36, 0.5),
+                                          (12, 2, 6, 8, 1.0)])
+def test_shared_output_form(seed, T, k, d, p):
+    from oracle.moe import combine_shared_ref
+    from oracle.numerics import bf16_bits_to_f64
+
+    y, rr, w, mask = _case(seed, T, k, d, p)
+    rng = np.random.default_rng(seed + 100)
+    shared = rng.standard_normal((T, d)).astype(np.float32)
+    out, ob = _run_shared(y, rr, w, mask, shared)
+    ref = combine_shared_ref(y, rr, w, mask, shared, T, k)
+    scale = np.abs(y).max() * np.abs(w).sum(axis=1).max() + np.abs(shared).max()
+    assert np.abs(out - ref).max() <= 1e-6 * scale
+    # bf16 copy: round to nearest of the sum, within the fp32 error of the sum
+    bf = bf16_bits_to_f64(ob)
+    half_ulp = np.ldexp(1.0, np.frexp(ref)[1] - 9)  # bf16 keeps 8 significant bits
+    assert np.all(np.abs(bf - ref) <= half_ulp * (1 + 1e-6) + 1e-6 * scale)
+    # without shared rows and with only the fp32 output it is the plain combine, bit for bit
+    plain, none = _run_shared(y, rr, w, mask, None, want_bf16=False)
+    assert none is None
+    assert np.array_equal(plain.view(np.uint32), _run(y, rr, w, mask).view(np.uint32))
+    # bf16 only
+    none2, ob2 = _run_shared(y, rr, w, mask, shared, want_fp32=False)
+    assert none2 is None and np.array_equal(ob2, ob)

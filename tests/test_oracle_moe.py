@@ -192,3 +192,25 @@ def test_rounding_point_of_h_is_observable():
         moe.nx.bf16_round = orig
     assert rel_frob(b, a) > 1e-3
     assert not math.isnan(rel_frob(b, a))
+
+
+def test_shared_output_combine_is_routed_plus_shared():
+    """Shared-output combine: the dense one-hot product plus the shared rows;
+    with no shared rows it is the plain combine."""
+    rng = np.random.default_rng(31)
+    T, k, d = 9, 4, 12
+    R = T * k
+    y = rng.standard_normal((R, d))
+    rr = rng.permutation(R).astype(np.int32)
+    w = rng.random((T, k))
+    mask = (rng.random((T, k)) > 0.3).astype(np.uint8)
+    shared = rng.standard_normal((T, d))
+    G = np.zeros((T, R))
+    for t in range(T):
+        for j in range(k):
+            if mask[t, j]:
+                G[t, rr[t * k + j]] += w[t, j]
+    ours = moe.combine_shared_ref(y, rr, w, mask, shared, T, k)
+    assert np.allclose(ours, G @ y + shared, rtol=1e-13, atol=1e-13)
+    plain = moe.combine_shared_ref(y, rr, w, mask, None, T, k)
+    assert np.array_equal(plain, moe.combine_ref(y, rr, w, mask, T, k))
