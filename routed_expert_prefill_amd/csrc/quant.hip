@@ -7,8 +7,9 @@
 // largest finite 448).  The pages define none of their own low-bit formats;
 // this is the format gfx950's fp8 MFMA consumes.
 //
-// One workgroup per row (rows of at most kQMaxCols elements are read once
-// into registers, reduced, then encoded and written).
+// Rows of up to 4096 elements: one wave per row; longer rows (up to
+// kQMaxCols): one workgroup per row.  Either way a row is read once into
+// registers, reduced, then encoded and written.
 #include "kernels.h"
 
 namespace moe {
@@ -102,10 +103,75 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
   }
 }
 
+// Rows of at most kQWaveMaxCols elements: one wave per row (four rows per
+// workgroup), lane l holding elements 8 l + 512 i .. +7, the row maximum
+// reduced with shuffles only.  Same arithmetic as quant_rows_kernel.
+constexpr int kQWaveMaxCols = 4096;
+constexpr int kQWaveLoads = kQWaveMaxCols / (kWave * 8);  // 16-byte loads per lane
+
+__global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
+    const uint16_t *__restrict__ x, int rows, const int32_t *rows_dev, int cols,
+    uint8_t *__restrict__ q, float *__restrict__ s) {
+  const int nrows = rows_dev ? *rows_dev : rows;
+  const int lane = lane_id();
+  const int waves = gridDim.x * (kQThreads / kWave);
+  for (int row = blockIdx.x * (kQThreads / kWave) + threadIdx.x / kWave; row < nrows; row += waves) {
+    const uint16_t *src = x + (size_t)row * cols;
+    i32x4 raw[kQWaveLoads];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQWaveLoads; ++i) {
+      const int c = (i * kWave + lane) * 8;  // cols is a multiple of 8
+      if (c < cols) {
+        raw[i] = *reinterpret_cast<const i32x4 *>(src + c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t two = (uint32_t)raw[i][w];
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two & 0xffffu))));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two >> 16))));
+        }
+      }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const bool zero = amax == 0.0f;
+    const float sc = zero ? 1.0f : amax / 448.0f;
+    if (lane == 0) s[row] = sc;
+    uint8_t *dst = q + (size_t)row * cols;
+#pragma unroll
+    for (int i = 0; i < kQWaveLoads; ++i) {
+      const int c = (i * kWave + lane) * 8;
+      if (c < cols) {
+        uint2 out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t two = (uint32_t)raw[i][h * 2 + (e >> 1)];
+            const uint16_t bits = (e & 1) ? (uint16_t)(two >> 16) : (uint16_t)(two & 0xffffu);
+            const uint32_t code = zero ? 0u : f32_to_e4m3(bf16_bits_to_f32(bits) / sc);
+            packed |= code << (8 * e);
+          }
+          (h ? out.y : out.x) = packed;
+        }
+        *reinterpret_cast<uint2 *>(dst + c) = out;
+      }
+    }
+  }
+}
+
 int quant_max_cols() { return kQMaxCols; }
 
 hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream) {
+  if (cols <= kQWaveMaxCols) {
+    const int per_block = kQThreads / kWave;
+    const long long want = ((long long)rows + per_block - 1) / per_block;
+    const int grid = (int)(want < grid_cap ? want : grid_cap);
+    hipLaunchKernelGGL(quant_rows_wave_kernel, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+                       stream, x, rows, rows_dev, cols, q, s);
+    return hipGetLastError();
+  }
   const int grid = rows < grid_cap ? rows : grid_cap;
   hipLaunchKernelGGL(quant_rows_kernel, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0, stream, x,
                      rows, rows_dev, cols, q, s);

@@ -20,12 +20,39 @@ def _gpu(xbits):
 
 
 @pytest.mark.parametrize("rows,cols,scale", [(64, 4096, 1.0), (37, 2048, 3e-3), (5, 128, 50.0),
-                                             (300, 16384, 1.0), (8, 256, 2.0 ** -60)])
+                                             (300, 16384, 1.0), (8, 256, 2.0 ** -60),
+                                             (3, 384, 1.0), (2, 4224, 1.0), (1031, 640, 7.0),
+                                             (4, 512, 2.0 ** -128), (4, 512, 2.0 ** 110)])
 def test_matches_oracle(rows, cols, scale):
     rng = np.random.default_rng(rows + cols)
     x = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
     x[0, :5] = [0.0, -0.0, 1e-30, -1e-30, 0.0]
     bits = f32_to_bf16_bits(x)
+    q, s = _gpu(bits)
+    qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+
+
+def test_values_on_and_near_rounding_boundaries():
+    """Quotients on and within a few ulp of E4M3 rounding boundaries (ties to
+    even, normal and subnormal ranges), for scales that are and are not
+    powers of two."""
+    rng = np.random.default_rng(12)
+    mids = np.array([432.0, 208.0, 17.0, 1.0625, 0.5 * 2.0 ** -9, 1.5 * 2.0 ** -9, 3.5 * 2.0 ** -9,
+                     2.0 ** -6 * 1.0625, 7.5 * 2.0 ** -9], np.float64)
+    rows = []
+    for amax in (448.0, 300.0, 1.0, 7.3e-3, 5.1e4):
+        sc = np.float32(np.float32(amax) / np.float32(448.0))
+        r = (mids[rng.integers(0, len(mids), 255)] * np.float64(sc) *
+             rng.choice([-1.0, 1.0], 255)).astype(np.float32)
+        row = np.concatenate([[np.float32(amax)], r]).astype(np.float32)
+        rows.append(row)
+    x = np.stack(rows)
+    bits = f32_to_bf16_bits(x)
+    # nudge some values by one bf16 ulp either way
+    bits[:, 1::3] += 1
+    bits[:, 2::3] -= 1
     q, s = _gpu(bits)
     qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
     assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
