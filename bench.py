@@ -193,7 +193,7 @@ def main():
              ten["w_up"], ten["w_down"], ten.get("s_gate"), ten.get("s_up"), ten.get("s_down"))
 
     def step(ev=None):
-        return run(*wargs, gate_up_events=ev)
+        return run(*wargs, stage_events=ev)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -216,10 +216,30 @@ def main():
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
-    gu_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    gu_ms = [a.elapsed_time(b) for a, b in evs]
     gu_avg = sum(gu_ms) / len(gu_ms)
+
+    # each call timed alone: a second pass of K steps (after the timed
+    # region) with events between the calls; per-step median/MAD/min from it
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(bev[i])
+    torch.cuda.synchronize(dev)
+    stage_names = ["route_build", "ffn_plan", "gate_up", "down", "combine"]
+    per_stage = {n: [e[i].elapsed_time(e[i + 1]) for e in bev] for i, n in enumerate(stage_names)}
+    per_step = [e[0].elapsed_time(e[5]) for e in bev]
+
+    def med(v):
+        v = sorted(v)
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+    step_med = med(per_step)
+    step_stats = {"median": round(step_med, 5), "mad": round(med([abs(v - step_med) for v in per_step]), 5),
+                  "min": round(min(per_step), 5)}
+    stages_ms = {n: round(med(v), 5) for n, v in per_stage.items()}
     log(f"whole path: {ms_step:.4f} ms/step (wall {1e3 * t_wall / args.steps:.4f}); "
-        f"gate/up stage avg {gu_avg:.4f} ms, median {gu_ms[len(gu_ms) // 2]:.4f} ms")
+        f"per step median {step_stats['median']:.4f} ms; stages {stages_ms}")
 
     counts = run.rt.counts.cpu().numpy()[: wl.E].tolist()
     work = algorithmic_work(wl, counts, wl.T)
@@ -291,6 +311,8 @@ def main():
                  "roofline_frac": round(t_path_roof / (ms_step / 1e3), 4),
                  "active_rows": work["R_act"], "experts_used": work["experts_used"],
                  "stage_bytes": work["stage_bytes"]},
+        "step_ms": step_stats,  # from the per-call pass, not the timed region
+        "stages_ms": stages_ms,
         "roofline": roof,
         "router": router,
         "cpu_baseline": cpu,

@@ -275,17 +275,32 @@ class MoEPrefill:
         self.out = torch.empty(T, d, dtype=torch.float32, device=dev)
 
     def __call__(self, x, topk_ids, topk_w, route_mask, w_gate, w_up, w_down, s_gate=None,
-                 s_up=None, s_down=None, gate_up_events=None):
-        """One pass of the path.  gate_up_events: optional (start, end) torch
-        events recorded on the current stream around the gate/up stage."""
+                 s_up=None, s_down=None, stage_events=None):
+        """One pass of the path.  stage_events: optional torch events recorded
+        on the current stream: 2 events around the gate/up stage, or 6 --
+        before the route build and after each of route build, FFN plan,
+        gate/up, down and combine."""
+        ev = stage_events
+        if ev is not None and len(ev) == 2:
+            ev = [None, None, ev[0], ev[1], None, None]  # around ffn_gate_up
+        if ev is not None and ev[0] is not None:
+            ev[0].record()
         rt = route_build(topk_ids, route_mask, self.E, out=self.rt, workspace=self.rb_ws)
-        if gate_up_events is None:
+        if ev is None:
             grouped_ffn(x, rt.offsets, rt.sorted_routes, w_gate, w_up, w_down, self.k, s_gate,
                         s_up, s_down, y=self.y, workspace=self.ffn_ws)
-        else:
-            ffn_plan(self.desc, x, rt.offsets, self.ffn_ws)
-            gate_up_events[0].record()
-            ffn_gate_up(self.desc, x, rt.sorted_routes, w_gate, w_up, s_gate, s_up, self.ffn_ws)
-            gate_up_events[1].record()
-            ffn_down(self.desc, rt.offsets, w_down, s_down, self.y, self.ffn_ws)
-        return combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out)
+            return combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out)
+        def mark(i):
+            if ev[i] is not None:
+                ev[i].record()
+
+        mark(1)
+        ffn_plan(self.desc, x, rt.offsets, self.ffn_ws)
+        mark(2)
+        ffn_gate_up(self.desc, x, rt.sorted_routes, w_gate, w_up, s_gate, s_up, self.ffn_ws)
+        mark(3)
+        ffn_down(self.desc, rt.offsets, w_down, s_down, self.y, self.ffn_ws)
+        mark(4)
+        out = combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out)
+        mark(5)
+        return out
