@@ -22,10 +22,18 @@ struct Tile {
   int e;
   int row0;
   int nrows;
-  int ablk;
+  int ablk;  // row capacity / 32 in the low byte, kTileStream flag above it
 };
 
 constexpr int kTileRows = 256;
+
+// Set on the only tile of an expert with at most kTileRows rows: its weights
+// are read by that tile's items alone, so they go through non-temporal loads
+// and leave the caches to the activation rows, which every item re-reads.
+// Experts with several tiles keep the default policy (their weights are
+// re-read once per tile).
+constexpr int kTileStream = 0x100;
+__device__ __forceinline__ int tile_class(const Tile &t) { return t.ablk & 0xff; }
 
 // Layout of the schedule at the start of the grouped-FFN workspace.
 struct Schedule {

@@ -82,7 +82,8 @@ __device__ __forceinline__ float block_scale(float lo, float hi, int s) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s & 63));
 }
 
-template <bool GATEUP, int AB>
+// NT: weight rows through non-temporal loads (tile flagged kTileStream).
+template <bool GATEUP, bool NT, int AB>
 __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0, uint8_t *ring,
                                         uint32_t ring_lds) {
   using L = G8Layout<AB>;
@@ -130,7 +131,11 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int i = wv + kG8Waves * j;
-      if (i < NL) dma16(src[j] + s * 128, base + (uint32_t)i * 1024u);
+      if (NT && i >= NA) {
+        if (i < NL) dma16_nt(src[j] + s * 128, base + (uint32_t)i * 1024u);
+      } else if (i < NL) {
+        dma16(src[j] + s * 128, base + (uint32_t)i * 1024u);
+      }
     }
   };
 
@@ -250,6 +255,15 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
   }
 }
 
+template <bool GATEUP, int AB>
+__device__ __forceinline__ void g8_item_any(const Gg8Args &a, const Tile &t, int n0, uint8_t *ring,
+                                            uint32_t ring_lds) {
+  if (t.ablk & kTileStream)
+    g8_item<GATEUP, true, AB>(a, t, n0, ring, ring_lds);
+  else
+    g8_item<GATEUP, false, AB>(a, t, n0, ring, ring_lds);
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kG8Ring];
@@ -268,11 +282,11 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
     const int ti = it / per_tile;
     const int n0 = (it - ti * per_tile) * FEAT;
     const Tile t = a.tiles[ti];
-    switch (t.ablk) {
-      case 8: g8_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
-      case 4: g8_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
-      case 2: g8_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
-      default: g8_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+    switch (tile_class(t)) {
+      case 8: g8_item_any<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
+      case 4: g8_item_any<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
+      case 2: g8_item_any<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
+      default: g8_item_any<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
     }
     // the ring (and the queue head in it) is rewritten only after every wave
     // has passed this barrier

@@ -100,12 +100,13 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     pos[c] += base;
     base += tot[c];
   }
+  const int stream = n <= kTileRows ? kTileStream : 0;  // the expert's only tile
   for (int i = 0; i < cnt[0]; ++i) {
     Tile t;
     t.e = e;
     t.row0 = row0 + i * kTileRows;
     t.nrows = min(kTileRows, n - i * kTileRows);
-    t.ablk = 8;
+    t.ablk = 8 | stream;
     tiles[pos[0] + i] = t;
   }
   if (rab > 0 && rab < 8) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     t.e = e;
     t.row0 = row0 + nfull * kTileRows;
     t.nrows = rem;
-    t.ablk = rab;
+    t.ablk = rab | stream;
     tiles[pos[c]] = t;
   }
   if (e == 0) {
@@ -160,7 +161,10 @@ struct GgLayout {
   __device__ static int wrow(int wv, int tw) { return 32 * AB + 32 * wtile(wv, tw); }
 };
 
-template <bool GATEUP, int AB, int WR = kGgWRows>
+// NT: weight rows go through non-temporal loads (the tile carries
+// kTileStream); a template parameter because a per-load choice inside the
+// stage loop cost the MFMA-bound tiles up to 4%.
+template <bool GATEUP, bool NT, int AB, int WR = kGgWRows>
 __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
                                         uint32_t ring_lds) {
   using L = GgLayout<AB, WR>;
@@ -209,7 +213,11 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int i = wv + kGgWaves * j;
-      if (i < NL) dma16(src[j] + s * 64, base + (uint32_t)i * 1024u);
+      if (NT && i >= NA) {
+        if (i < NL) dma16_nt(src[j] + s * 64, base + (uint32_t)i * 1024u);
+      } else if (i < NL) {
+        dma16(src[j] + s * 64, base + (uint32_t)i * 1024u);
+      }
     }
   };
 
@@ -287,6 +295,15 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
   }
 }
 
+template <bool GATEUP, int AB, int WR = kGgWRows>
+__device__ __forceinline__ void gg_item_any(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
+                                            uint32_t ring_lds) {
+  if (t.ablk & kTileStream)
+    gg_item<GATEUP, true, AB, WR>(a, t, n0, ring, ring_lds);
+  else
+    gg_item<GATEUP, false, AB, WR>(a, t, n0, ring, ring_lds);
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <bool GATEUP>
@@ -311,15 +328,15 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
     const int n0 = (it - ti * per_tile) * FEAT;
     const Tile t = a.tiles[ti];
     if (a.wr == 128) {
-      gg_item<GATEUP, 1, 128>(a, t, n0, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 128>(a, t, n0, ring, ring_lds);
     } else if (a.wr == 64) {
-      gg_item<GATEUP, 1, 64>(a, t, n0, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 64>(a, t, n0, ring, ring_lds);
     } else {
-      switch (t.ablk) {
-        case 8: gg_item<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
-        case 4: gg_item<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
-        case 2: gg_item<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
-        default: gg_item<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+      switch (tile_class(t)) {
+        case 8: gg_item_any<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
+        case 4: gg_item_any<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
+        case 2: gg_item_any<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
+        default: gg_item_any<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
       }
     }
     // the ring (and the queue head in it) is rewritten only after every wave
