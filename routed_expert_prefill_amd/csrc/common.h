@@ -39,7 +39,8 @@ __device__ __forceinline__ int tile_class(const Tile &t) { return t.ablk & 0xff;
 struct Schedule {
   int n_tiles;     // entries of the tile list, tallest capacity first
   int counter[2];  // work-queue heads of the gate/up and down kernels
-  int pad[61];     // keeps the tile list 256-byte aligned
+  int n_small;     // 32-row tiles, the last n_small entries of the list
+  int pad[60];     // keeps the tile list 256-byte aligned
 };
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l

@@ -42,6 +42,9 @@ struct GgArgs {
   const int *ntiles;
   int *counter;        // item queue head, zeroed by the schedule
   int wr;              // weight rows per item: 256, or 128 / 64 when every tile holds <= 32 rows
+  int nb;              // feature blocks per item (streamed through one ring fill)
+  int nb_skinny;       // the same for 32-row tiles when nearly all tiles are 32-row ones
+  const int *n_small;  // 32-row tiles at the end of the tile list
 };
 
 constexpr int kGgThreads = 512;
@@ -122,6 +125,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     sch->n_tiles = base;
     sch->counter[0] = 0;
     sch->counter[1] = 0;
+    sch->n_small = tot[3];
   }
 }
 
@@ -164,10 +168,14 @@ struct GgLayout {
 // NT: weight rows go through non-temporal loads (the tile carries
 // kTileStream); a template parameter because a per-load choice inside the
 // stage loop cost the MFMA-bound tiles up to 4%.
-template <bool GATEUP, bool NT, int AB, int WR = kGgWRows>
-__device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
-                                        uint32_t ring_lds) {
+// MB: the item may carry several feature blocks (nb); without it nb is 1 and
+// the stage loop has no block bookkeeping.
+template <bool GATEUP, bool NT, bool MB, int AB, int WR = kGgWRows>
+__device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, int nb_arg,
+                                        uint8_t *ring, uint32_t ring_lds) {
+  const int nb = MB ? nb_arg : 1;
   using L = GgLayout<AB, WR>;
+  constexpr int FEAT = GATEUP ? WR / 2 : WR;  // output features per block
   constexpr int TT = L::TT, TW = L::TW;
   constexpr int NA = 4 * AB;       // activation loads (8 rows each) per stage
   constexpr int NL = NA + WR / 8;  // all loads per stage
@@ -208,15 +216,21 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
   }
   constexpr int NS = GgRing<AB, WR>::kDepth;
   constexpr int SLOT = GgRing<AB, WR>::kSlot;
-  auto issue = [&](int s, int slot) {
+  // stage s of feature block b: weight rows move on by FEAT rows per block,
+  // activation rows stay
+  const size_t bstep = (size_t)FEAT * K;
+  auto issue = [&](int s, int b, int slot) {
     const uint32_t base = ring_lds + (uint32_t)(slot * SLOT);
+    const size_t woff = MB ? (size_t)b * bstep : 0;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int i = wv + kGgWaves * j;
+      const uint16_t *p = src[j] + s * 64;
+      if (MB && i >= NA) p += woff;
       if (NT && i >= NA) {
-        if (i < NL) dma16_nt(src[j] + s * 64, base + (uint32_t)i * 1024u);
+        if (i < NL) dma16_nt(p, base + (uint32_t)i * 1024u);
       } else if (i < NL) {
-        dma16(src[j] + s * 64, base + (uint32_t)i * 1024u);
+        dma16(p, base + (uint32_t)i * 1024u);
       }
     }
   };
@@ -229,26 +243,45 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
   for (int ks = 0; ks < 4; ++ks) lane_off[ks] = rr * 128 + ring_slot(rr, 2 * ks + rh) * 16;
 
   f32x16 acc[TW][TT];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int tw = 0; tw < TW; ++tw)
+    for (int tw = 0; tw < TW; ++tw)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+        for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+  };
+  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
+  auto epilogue = [&](int nb0) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = L::arow(wv, tt) + rr;
+      if (row < t.nrows) {
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+          const int wt = L::wtile(wv, tw);
+          if (GATEUP) {
+            // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const int n = nb0 + wt * 16 + g * 8 + rh * 4;
+              gg_store<true>(a, t.row0 + row, n, quad(acc[tw][tt], g), quad(acc[tw][tt], g + 2));
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = nb0 + wt * 32 + g * 8 + rh * 4;
+              if (n < a.N) gg_store<false>(a, t.row0 + row, n, quad(acc[tw][tt], g), f32x4{});
+            }
+          }
+        }
+      }
+    }
+  };
+  zero_acc();
 
-  wait_vm(0);
-  ring_barrier();  // every wave is done with the ring contents of the previous item
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s, s);
-  int slot = 0;
-  for (int s = 0; s < nst; ++s) {
-    // this wave's loads of stage s are done; later stages may stay in flight
-    wait_vm(cnt * min(NS - 2, nst - 1 - s));
-    ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
-    const int ahead = s + NS - 1;
-    if (ahead < nst) issue(ahead, slot == 0 ? NS - 1 : slot - 1);
-    const uint8_t *buf = ring + slot * SLOT;
+  // the MFMAs of one ring stage
+  auto mma_stage = [&](const uint8_t *buf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (!L::active(wv)) break;
@@ -264,44 +297,70 @@ __device__ __forceinline__ void gg_item(const GgArgs &a, const Tile &t, int n0, 
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[tw][tt] = mfma32_bf16(fw[tw], fa[tt], acc[tw][tt]);
     }
-    slot = slot == NS - 1 ? 0 : slot + 1;
-  }
+  };
 
-  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
-  if (!L::active(wv)) return;
+  wait_vm(0);
+  ring_barrier();  // every wave is done with the ring contents of the previous item
+  if constexpr (!MB) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int row = L::arow(wv, tt) + rr;
-    if (row < t.nrows) {
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nst) issue(s, 0, s);
+    int slot = 0;
+    for (int s = 0; s < nst; ++s) {
+      // this wave's loads of stage s are done; later stages may stay in flight
+      wait_vm(cnt * min(NS - 2, nst - 1 - s));
+      ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
+      const int ahead = s + NS - 1;
+      if (ahead < nst) issue(ahead, 0, slot == 0 ? NS - 1 : slot - 1);
+      mma_stage(ring + slot * SLOT);
+      slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    if (L::active(wv)) epilogue(n0);
+  } else {
+    // nb feature blocks of nst stages each run through the ring back to
+    // back; a block's results are written while the next block's first
+    // stages load
+    const int total = nb * nst;
+    int ib = 0, is = 0;  // block and stage of the next stage to load
+    auto issue_next = [&](int slot) {
+      issue(is, ib, slot);
+      if (++is == nst) {
+        is = 0;
+        ++ib;
+      }
+    };
 #pragma unroll
-      for (int tw = 0; tw < TW; ++tw) {
-        const int wt = L::wtile(wv, tw);
-        if (GATEUP) {
-          // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const int n = n0 + wt * 16 + g * 8 + rh * 4;
-            gg_store<true>(a, t.row0 + row, n, quad(acc[tw][tt], g), quad(acc[tw][tt], g + 2));
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wt * 32 + g * 8 + rh * 4;
-            if (n < a.N) gg_store<false>(a, t.row0 + row, n, quad(acc[tw][tt], g), f32x4{});
-          }
-        }
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < total) issue_next(s);
+    int slot = 0, cb = 0, cs = 0;  // block and stage being multiplied
+    for (int sg = 0; sg < total; ++sg) {
+      // as above; stores of an earlier block, counted too, only make the
+      // wait longer
+      wait_vm(cnt * min(NS - 2, total - 1 - sg));
+      ring_barrier();
+      if (sg + NS - 1 < total) issue_next(slot == 0 ? NS - 1 : slot - 1);
+      mma_stage(ring + slot * SLOT);
+      slot = slot == NS - 1 ? 0 : slot + 1;
+      if (++cs == nst) {
+        if (L::active(wv)) epilogue(n0 + cb * FEAT);
+        cs = 0;
+        ++cb;
+        if (cb < nb) zero_acc();
       }
     }
   }
 }
 
 template <bool GATEUP, int AB, int WR = kGgWRows>
-__device__ __forceinline__ void gg_item_any(const GgArgs &a, const Tile &t, int n0, uint8_t *ring,
-                                            uint32_t ring_lds) {
+__device__ __forceinline__ void gg_item_any(const GgArgs &a, const Tile &t, int n0, int nb,
+                                            uint8_t *ring, uint32_t ring_lds) {
+  // several feature blocks per item only for the down projection: the
+  // block bookkeeping slowed the MFMA-bound gate/up items
+  constexpr bool MB = !GATEUP;
   if (t.ablk & kTileStream)
-    gg_item<GATEUP, true, AB, WR>(a, t, n0, ring, ring_lds);
+    gg_item<GATEUP, true, MB, AB, WR>(a, t, n0, nb, ring, ring_lds);
   else
-    gg_item<GATEUP, false, AB, WR>(a, t, n0, ring, ring_lds);
+    gg_item<GATEUP, false, MB, AB, WR>(a, t, n0, nb, ring, ring_lds);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -315,8 +374,17 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   // output features per item: half the weight rows for gate/up (gate and up
   // rows of the same features), all of them for down
   const int FEAT = GATEUP ? a.wr / 2 : a.wr;
-  const int per_tile = (a.N + FEAT - 1) / FEAT;
-  const int total = *a.ntiles * per_tile;
+  // items of taller tiles first (the list is tallest first), then of the
+  // 32-row tiles; the 32-row tiles take nb_skinny blocks per item when the
+  // taller ones are at most an eighth as many (on MI355X, 4 blocks were
+  // best there and 2 elsewhere, for 200 to 8192 tokens)
+  const int nsmall = *a.n_small;
+  const int nbig = *a.ntiles - nsmall;
+  const int nbs = nbig * 8 <= nsmall ? a.nb_skinny : a.nb;
+  const int FIB = FEAT * a.nb, FIS = FEAT * nbs;  // output features per item
+  const int ptb = (a.N + FIB - 1) / FIB, pts = (a.N + FIS - 1) / FIS;
+  const int items_big = nbig * ptb;
+  const int total = items_big + nsmall * pts;
   for (;;) {
     if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
     __syncthreads();
@@ -324,19 +392,30 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
     // so the tile fetch below is a scalar load
     const int it = __builtin_amdgcn_readfirstlane(*next_item);
     if (it >= total) break;
-    const int ti = it / per_tile;
-    const int n0 = (it - ti * per_tile) * FEAT;
+    int ti, n0, nbw;
+    if (it < items_big) {
+      ti = it / ptb;
+      n0 = (it - ti * ptb) * FIB;
+      nbw = a.nb;
+    } else {
+      const int is = it - items_big;
+      const int q = is / pts;
+      ti = nbig + q;
+      n0 = (is - q * pts) * FIS;
+      nbw = nbs;
+    }
+    const int nb = min(nbw, (a.N - n0 + FEAT - 1) / FEAT);
     const Tile t = a.tiles[ti];
     if (a.wr == 128) {
-      gg_item_any<GATEUP, 1, 128>(a, t, n0, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 128>(a, t, n0, nb, ring, ring_lds);
     } else if (a.wr == 64) {
-      gg_item_any<GATEUP, 1, 64>(a, t, n0, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 64>(a, t, n0, nb, ring, ring_lds);
     } else {
       switch (tile_class(t)) {
-        case 8: gg_item_any<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
-        case 4: gg_item_any<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
-        case 2: gg_item_any<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
-        default: gg_item_any<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+        case 8: gg_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
+        case 4: gg_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
+        case 2: gg_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
+        default: gg_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;
       }
     }
     // the ring (and the queue head in it) is rewritten only after every wave
@@ -380,6 +459,14 @@ static int item_weight_rows(const FfnLaunch &L, int n_out, int mats) {
   return best;
 }
 
+// Feature blocks per item: more than one only for full-width items (narrow
+// items exist to make more of them) and when the blocks tile the output
+// features exactly.
+static int item_blocks(int wr, int n_out, int mats, int want) {
+  const int feat = wr / mats;
+  return (want > 1 && wr == kGgWRows && n_out % (feat * want) == 0) ? want : 1;
+}
+
 hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream) {
   if (stages & kStagePlan) {
     const hipError_t err = launch_grouped_schedule(L.offsets, L.E, L.sch, L.tiles, stream);
@@ -389,6 +476,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
   g.k = L.k;
   g.tiles = L.tiles;
   g.ntiles = &L.sch->n_tiles;
+  g.n_small = &L.sch->n_small;
   if (stages & kStageGateUp) {
     g.act = L.x;
     g.sorted_routes = L.sorted_routes;
@@ -399,6 +487,8 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.d;
     g.counter = &L.sch->counter[0];
     g.wr = item_weight_rows(L, L.f, 2);
+    g.nb = 1;
+    g.nb_skinny = 1;
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(L.num_cus), dim3(kGgThreads), 0, stream, g);
   }
   if (stages & kStageDown) {
@@ -411,6 +501,8 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.f;
     g.counter = &L.sch->counter[1];
     g.wr = item_weight_rows(L, L.d, 1);
+    g.nb = item_blocks(g.wr, L.d, 1, 2);
+    g.nb_skinny = item_blocks(g.wr, L.d, 1, 4);
     hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(L.num_cus), dim3(kGgThreads), 0, stream,
                        g);
   }
