@@ -149,6 +149,32 @@ def test_decode_sized_chunks(T, d, f, seed):
     assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
 
 
+SKINNY_COUNTS = [1, 5, 9, 17, 20, 24, 28, 31, 32, 3, 12, 7, 0, 30, 26, 15]
+MIXED_COUNTS = [40, 70, 130, 300, 10, 20, 5, 64, 200, 33, 1, 2, 0, 513]
+
+
+@pytest.mark.parametrize("counts", ["skinny", "mixed"])
+@pytest.mark.parametrize("d", [1024, 1536])
+def test_feature_blocks_per_item(counts, d):
+    """Down-projection items of one, two and four feature blocks of 256
+    outputs: only 32-row tiles ("skinny") or many taller tiles ("mixed"),
+    with d = 1024 (blocks of 512 and 1024 outputs tile it) and d = 1536 (only
+    512 does).  Every active row of y is written, every masked row is not."""
+    cnt = SKINNY_COUNTS if counts == "skinny" else MIXED_COUNTS
+    E, f = len(cnt), 256
+    ids, mask = routing_with_counts(cnt, 6, seed=30, masked_extra=9)
+    T, k = ids.shape
+    w = np.random.default_rng(31).random((T, k)).astype(np.float32)
+    x = _x(T, d, 32)
+    W = _weights(E, d, f, False, 33)
+    run, out = _run(ids, w, mask, x, W, E, False, y_fill=float("nan"))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E)
+    _check(out, ref, BF16_TOL)
+    n_act = int(run.rt.offsets[E].item())
+    y = run.y.cpu().numpy()
+    assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
+
+
 def test_single_expert_single_route_is_dense_mlp():
     """E = 1, k = 1, gate 1, no mask: a dense SwiGLU MLP, checked also against
     torch's own matmul on the GPU (an independent library product)."""
