@@ -29,9 +29,11 @@ struct Gg8Args {
   const Tile *tiles;
   const int *ntiles;
   int *counter;
+  int nb;  // feature blocks per item (streamed through one ring fill)
 };
 
 constexpr int kG8Threads = 512;
+constexpr int kG8MaxBlocks = 4;
 constexpr int kG8Waves = kG8Threads / kWave;
 constexpr int kG8WRows = 128;
 constexpr int kG8Ring = 160 * 1024;
@@ -83,10 +85,15 @@ __device__ __forceinline__ float block_scale(float lo, float hi, int s) {
 }
 
 // NT: weight rows through non-temporal loads (tile flagged kTileStream).
-template <bool GATEUP, bool NT, int AB>
-__device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0, uint8_t *ring,
-                                        uint32_t ring_lds) {
+// MB: the item may carry up to kG8MaxBlocks feature blocks (nb) of 128
+// outputs; without it nb is 1 and the stage loop has no block bookkeeping.
+template <bool GATEUP, bool NT, bool MB, int AB>
+__device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0, int nb_arg,
+                                        uint8_t *ring, uint32_t ring_lds) {
   using L = G8Layout<AB>;
+  constexpr int FEAT = GATEUP ? 64 : 128;  // output features per block
+  constexpr int NB = MB ? kG8MaxBlocks : 1;
+  const int nb = MB ? nb_arg : 1;
   constexpr int TT = L::TT, TW = L::TW;
   constexpr int NA = 4 * AB;             // activation loads (8 rows each) per stage
   constexpr int NL = NA + kG8WRows / 8;  // all loads per stage
@@ -126,28 +133,55 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
       src[j] = w + ((size_t)t.e * a.N + n) * K + lq * 16;
     }
   }
-  auto issue = [&](int s, int slot) {
+  // stage s of feature block b: weight rows move on by FEAT rows per block,
+  // activation rows stay
+  const size_t bstep = (size_t)FEAT * K;
+  auto issue = [&](int s, int b, int slot) {
     const uint32_t base = ring_lds + (uint32_t)(slot * SLOT);
+    const size_t woff = MB ? (size_t)b * bstep : 0;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int i = wv + kG8Waves * j;
+      const uint8_t *p = src[j] + s * 128;
+      if (MB && i >= NA) p += woff;
       if (NT && i >= NA) {
-        if (i < NL) dma16_nt(src[j] + s * 128, base + (uint32_t)i * 1024u);
+        if (i < NL) dma16_nt(p, base + (uint32_t)i * 1024u);
       } else if (i < NL) {
-        dma16(src[j] + s * 128, base + (uint32_t)i * 1024u);
+        dma16(p, base + (uint32_t)i * 1024u);
       }
     }
   };
 
-  // the item's weight rows all lie in one 128-row scale block
+  // Everything the item reads besides the ring is loaded here, before the
+  // ring fill: a compiler-tracked load between stages would make the
+  // compiler wait for every load in flight, the ring's included.
+  // Block scales: each 128-row scale block of the item's weight rows (one per
+  // feature block; gate/up items lie in one), the K / 128 scales of a row
+  // held two per lane.
   const int KB = nst;
-  const size_t srow = ((size_t)t.e * (a.N / 128) + n0 / 128) * KB;
-  float sc0[2], sc1[2];
+  float sc0[NB][2], sc1[2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const size_t srow = ((size_t)t.e * (a.N / 128) + (n0 + b * FEAT) / 128) * KB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = lane + 64 * h;
+      sc0[b][h] = (b < nb && kb < KB) ? a.s0[srow + kb] : 0.f;
+    }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int kb = lane + 64 * h;
-    sc0[h] = kb < KB ? a.s0[srow + kb] : 0.f;
+    const size_t srow = ((size_t)t.e * (a.N / 128) + n0 / 128) * KB;
     sc1[h] = (GATEUP && kb < KB) ? a.s1[srow + kb] : 0.f;
+  }
+  // activation row scales of this lane's rows
+  float rsc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int row = L::atile(wv, tt) * 32 + (lane & 31);
+    const int i = t.row0 + min(row, t.nrows - 1);
+    rsc[tt] = a.act_scale[GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i];
   }
 
   // reader: row (lane & 31) of a 32-row tile; 64-element step ks takes the
@@ -161,94 +195,144 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
   }
 
   f32x16 acc[TW][TT];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int tw = 0; tw < TW; ++tw)
+    for (int tw = 0; tw < TW; ++tw)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+        for (int j = 0; j < 16; ++j) acc[tw][tt][j] = 0.f;
+  };
+  zero_acc();
   const bool on = L::active(wv);
+
+  // the MFMAs of stage s of a block whose weight scales are (lo, hi)
+  auto mma_stage = [&](const uint8_t *buf, int s, float lo, float hi) {
+    const float sg = block_scale(lo, hi, s);
+    const float su = GATEUP ? block_scale(sc1[0], sc1[1], s) : sg;
+    i32x8 fa[TT][2], fw[TW][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint8_t *r = buf + L::atile(wv, tt) * 32 * 128;
+        fa[tt][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
+      }
+#pragma unroll
+      for (int tw = 0; tw < TW; ++tw) {
+        const uint8_t *r = buf + (32 * AB + L::wtile(wv, tw) * 32) * 128;
+        fw[tw][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
+      }
+    }
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        f32x16 p;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = 0.f;
+        p = mfma32_fp8(fw[tw][0], fa[tt][0], p);
+        p = mfma32_fp8(fw[tw][1], fa[tt][1], p);
+        // gate/up: registers 0-7 hold gate rows of the tile, 8-15 up rows
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          acc[tw][tt][j] = __builtin_fmaf((GATEUP && j >= 8) ? su : sg, p[j], acc[tw][tt][j]);
+      }
+  };
+
+  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
+  auto epilogue = [&](int nb0) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = L::atile(wv, tt) * 32 + rr;
+      if (row < t.nrows) {
+        const int i = t.row0 + row;
+        const float rs = rsc[tt];
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+          const int wt = L::wtile(wv, tw);
+          if (GATEUP) {
+            // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const f32x4 gv = quad_scaled(acc[tw][tt], g, rs);
+              const f32x4 uv = quad_scaled(acc[tw][tt], g + 2, rs);
+              uint2 v;
+              v.x = (uint32_t)f32_to_bf16_bits(swiglu(gv[0], uv[0])) |
+                    ((uint32_t)f32_to_bf16_bits(swiglu(gv[1], uv[1])) << 16);
+              v.y = (uint32_t)f32_to_bf16_bits(swiglu(gv[2], uv[2])) |
+                    ((uint32_t)f32_to_bf16_bits(swiglu(gv[3], uv[3])) << 16);
+              const int n = nb0 + wt * 16 + g * 8 + rh * 4;
+              *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)i * a.N + n) = v;
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = nb0 + wt * 32 + g * 8 + rh * 4;
+              if (n < a.N)
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (size_t)i * a.N + n) =
+                    quad_scaled(acc[tw][tt], g, rs);
+            }
+          }
+        }
+      }
+    }
+  };
 
   wait_vm(0);
   ring_barrier();  // every wave is done with the ring contents of the previous item
+  if constexpr (!MB) {
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s, s);
-  int slot = 0;
-  for (int s = 0; s < nst; ++s) {
-    wait_vm(cnt * min(NS - 2, nst - 1 - s));
-    ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
-    const int ahead = s + NS - 1;
-    if (ahead < nst) issue(ahead, slot == 0 ? NS - 1 : slot - 1);
-    if (on) {
-      const uint8_t *buf = ring + slot * SLOT;
-      const float sg = block_scale(sc0[0], sc0[1], s);
-      const float su = GATEUP ? block_scale(sc1[0], sc1[1], s) : sg;
-      i32x8 fa[TT][2], fw[TW][2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const uint8_t *r = buf + L::atile(wv, tt) * 32 * 128;
-          fa[tt][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
-        }
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-          const uint8_t *r = buf + (32 * AB + L::wtile(wv, tw) * 32) * 128;
-          fw[tw][ks] = lds_i32x8(r + off0[ks], r + off1[ks]);
-        }
-      }
-#pragma unroll
-      for (int tw = 0; tw < TW; ++tw)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          f32x16 p;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) p[j] = 0.f;
-          p = mfma32_fp8(fw[tw][0], fa[tt][0], p);
-          p = mfma32_fp8(fw[tw][1], fa[tt][1], p);
-          // gate/up: registers 0-7 hold gate rows of the tile, 8-15 up rows
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            acc[tw][tt][j] = __builtin_fmaf((GATEUP && j >= 8) ? su : sg, p[j], acc[tw][tt][j]);
-        }
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nst) issue(s, 0, s);
+    int slot = 0;
+    for (int s = 0; s < nst; ++s) {
+      wait_vm(cnt * min(NS - 2, nst - 1 - s));
+      ring_barrier();  // stage s is in LDS for everyone; stage s - 1 is consumed
+      const int ahead = s + NS - 1;
+      if (ahead < nst) issue(ahead, 0, slot == 0 ? NS - 1 : slot - 1);
+      if (on) mma_stage(ring + slot * SLOT, s, sc0[0][0], sc0[0][1]);
+      slot = slot == NS - 1 ? 0 : slot + 1;
     }
-    slot = slot == NS - 1 ? 0 : slot + 1;
-  }
-
-  if (!on) return;
-  // register j of a 32x32 tile holds weight row 8*(j/4) + 4*rh + j%4, activation row rr
+    if (on) epilogue(n0);
+  } else {
+    // nb feature blocks of nst stages each run through the ring back to
+    // back; a block's results are written while the next block's first
+    // stages load
+    const int total = nb * nst;
+    int ib = 0, is = 0;  // block and stage of the next stage to load
+    auto issue_next = [&](int slot) {
+      issue(is, ib, slot);
+      if (++is == nst) {
+        is = 0;
+        ++ib;
+      }
+    };
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int row = L::atile(wv, tt) * 32 + rr;
-    if (row < t.nrows) {
-      const int i = t.row0 + row;
-      const float rs = a.act_scale[GATEUP ? (size_t)(a.sorted_routes[i] / a.k) : (size_t)i];
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < total) issue_next(s);
+    int slot = 0, cb = 0, cs = 0;  // block and stage being multiplied
+    float lo = sc0[0][0], hi = sc0[0][1];
+    for (int sg = 0; sg < total; ++sg) {
+      // as above; stores of an earlier block, counted too, only make the
+      // wait longer
+      wait_vm(cnt * min(NS - 2, total - 1 - sg));
+      ring_barrier();
+      if (sg + NS - 1 < total) issue_next(slot == 0 ? NS - 1 : slot - 1);
+      if (on) mma_stage(ring + slot * SLOT, cs, lo, hi);
+      slot = slot == NS - 1 ? 0 : slot + 1;
+      if (++cs == nst) {
+        if (on) epilogue(n0 + cb * FEAT);
+        cs = 0;
+        ++cb;
+        if (cb < nb) {
+          zero_acc();
 #pragma unroll
-      for (int tw = 0; tw < TW; ++tw) {
-        const int wt = L::wtile(wv, tw);
-        if (GATEUP) {
-          // rows 0-15 of the tile are gate features 16 wt + [0,16), rows 16-31 the same up features
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const f32x4 gv = quad_scaled(acc[tw][tt], g, rs);
-            const f32x4 uv = quad_scaled(acc[tw][tt], g + 2, rs);
-            uint2 v;
-            v.x = (uint32_t)f32_to_bf16_bits(swiglu(gv[0], uv[0])) |
-                  ((uint32_t)f32_to_bf16_bits(swiglu(gv[1], uv[1])) << 16);
-            v.y = (uint32_t)f32_to_bf16_bits(swiglu(gv[2], uv[2])) |
-                  ((uint32_t)f32_to_bf16_bits(swiglu(gv[3], uv[3])) << 16);
-            const int n = n0 + wt * 16 + g * 8 + rh * 4;
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)i * a.N + n) = v;
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wt * 32 + g * 8 + rh * 4;
-            if (n < a.N)
-              *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (size_t)i * a.N + n) =
-                  quad_scaled(acc[tw][tt], g, rs);
-          }
+          for (int b = 1; b < NB; ++b)
+            if (b == cb) {
+              lo = sc0[b][0];
+              hi = sc0[b][1];
+            }
         }
       }
     }
@@ -256,12 +340,14 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
 }
 
 template <bool GATEUP, int AB>
-__device__ __forceinline__ void g8_item_any(const Gg8Args &a, const Tile &t, int n0, uint8_t *ring,
-                                            uint32_t ring_lds) {
+__device__ __forceinline__ void g8_item_any(const Gg8Args &a, const Tile &t, int n0, int nb,
+                                            uint8_t *ring, uint32_t ring_lds) {
+  // several feature blocks per item only for the down projection
+  constexpr bool MB = !GATEUP;
   if (t.ablk & kTileStream)
-    g8_item<GATEUP, true, AB>(a, t, n0, ring, ring_lds);
+    g8_item<GATEUP, true, MB, AB>(a, t, n0, nb, ring, ring_lds);
   else
-    g8_item<GATEUP, false, AB>(a, t, n0, ring, ring_lds);
+    g8_item<GATEUP, false, MB, AB>(a, t, n0, nb, ring, ring_lds);
 }
 
 template <bool GATEUP>
@@ -270,9 +356,16 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
   // the queue head is passed through the idle ring between items
   int *next_item = reinterpret_cast<int *>(ring);
   const uint32_t ring_lds = lds_addr(ring);
-  constexpr int FEAT = GATEUP ? 64 : 128;  // output features per item
-  const int per_tile = (a.N + FEAT - 1) / FEAT;
-  const int total = *a.ntiles * per_tile;
+  constexpr int FEAT = GATEUP ? 64 : 128;  // output features per block
+  // blocks per item: halved while fewer than half the workgroups would get
+  // an item (counts above one divide the feature blocks of a tile)
+  const int ntiles = *a.ntiles;
+  const int pt1 = (a.N + FEAT - 1) / FEAT;
+  int nbi = a.nb;
+  while (nbi > 1 && 2 * ntiles * (pt1 / nbi) < (int)gridDim.x) nbi >>= 1;
+  const int FI = FEAT * nbi;  // output features per item
+  const int per_tile = (a.N + FI - 1) / FI;
+  const int total = ntiles * per_tile;
   for (;;) {
     if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
     __syncthreads();
@@ -280,13 +373,14 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
     const int it = __builtin_amdgcn_readfirstlane(*next_item);
     if (it >= total) break;
     const int ti = it / per_tile;
-    const int n0 = (it - ti * per_tile) * FEAT;
+    const int n0 = (it - ti * per_tile) * FI;
+    const int nb = min(nbi, (a.N - n0 + FEAT - 1) / FEAT);
     const Tile t = a.tiles[ti];
     switch (tile_class(t)) {
-      case 8: g8_item_any<GATEUP, 8>(a, t, n0, ring, ring_lds); break;
-      case 4: g8_item_any<GATEUP, 4>(a, t, n0, ring, ring_lds); break;
-      case 2: g8_item_any<GATEUP, 2>(a, t, n0, ring, ring_lds); break;
-      default: g8_item_any<GATEUP, 1>(a, t, n0, ring, ring_lds); break;
+      case 8: g8_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
+      case 4: g8_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
+      case 2: g8_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
+      default: g8_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;
     }
     // the ring (and the queue head in it) is rewritten only after every wave
     // has passed this barrier
@@ -318,6 +412,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.N = L.f;
     g.K = L.d;
     g.counter = &L.sch->counter[0];
+    g.nb = 1;
     hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
     err = hipGetLastError();
@@ -338,6 +433,10 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.N = L.d;
     g.K = L.f;
     g.counter = &L.sch->counter[1];
+    // the most blocks of 128 outputs, up to kG8MaxBlocks, that tile d
+    // (MI355X, 8192 tokens: down 0.946 -> 0.877 ms with four, 0.884 with two)
+    g.nb = kG8MaxBlocks;
+    while (g.nb > 1 && L.d % (128 * g.nb) != 0) g.nb >>= 1;
     hipLaunchKernelGGL(grouped_gemm8_kernel<false>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
   }

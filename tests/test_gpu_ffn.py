@@ -153,23 +153,26 @@ SKINNY_COUNTS = [1, 5, 9, 17, 20, 24, 28, 31, 32, 3, 12, 7, 0, 30, 26, 15]
 MIXED_COUNTS = [40, 70, 130, 300, 10, 20, 5, 64, 200, 33, 1, 2, 0, 513]
 
 
-@pytest.mark.parametrize("counts", ["skinny", "mixed"])
-@pytest.mark.parametrize("d", [1024, 1536])
-def test_feature_blocks_per_item(counts, d):
-    """Down-projection items of one, two and four feature blocks of 256
-    outputs: only 32-row tiles ("skinny") or many taller tiles ("mixed"),
-    with d = 1024 (blocks of 512 and 1024 outputs tile it) and d = 1536 (only
-    512 does).  Every active row of y is written, every masked row is not."""
+@pytest.mark.parametrize("fp8,counts,d", [
+    (False, "skinny", 1024), (False, "mixed", 1024), (False, "skinny", 1536), (False, "mixed", 1536),
+    (True, "mixed", 384), (True, "mixed", 768), (True, "skinny", 1024)])
+def test_feature_blocks_per_item(fp8, counts, d):
+    """Down-projection items of one, two and four feature blocks: only 32-row
+    tiles ("skinny") or many taller tiles ("mixed").  bf16 blocks are 256
+    outputs: d = 1024 is tiled by items of 512 and 1024 outputs, d = 1536
+    only by 512.  fp8 blocks are 128 outputs, each with its own row of weight
+    block scales: d = 384 takes one block per item, 768 two, 1024 four.
+    Every active row of y is written, every masked row is not."""
     cnt = SKINNY_COUNTS if counts == "skinny" else MIXED_COUNTS
     E, f = len(cnt), 256
     ids, mask = routing_with_counts(cnt, 6, seed=30, masked_extra=9)
     T, k = ids.shape
     w = np.random.default_rng(31).random((T, k)).astype(np.float32)
     x = _x(T, d, 32)
-    W = _weights(E, d, f, False, 33)
-    run, out = _run(ids, w, mask, x, W, E, False, y_fill=float("nan"))
-    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E)
-    _check(out, ref, BF16_TOL)
+    W = _weights(E, d, f, fp8, 33)
+    run, out = _run(ids, w, mask, x, W, E, fp8, y_fill=float("nan"))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
     n_act = int(run.rt.offsets[E].item())
     y = run.y.cpu().numpy()
     assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
