@@ -8,6 +8,14 @@
       WRITE_SIZE run (--output-format csv), each scaled by what the same
       counter reads for the 1 GiB device copy that bench.py --copy-calibration
       runs in the same process; records the kernel source hash bench.py checks.
+  python -m routed_expert_prefill_amd.profiling mfma --csv <csv> --kernel <name prefix>
+          [--avg-us <average duration from a kernel trace>]
+      MFMA counters per launch of one kernel from a run with
+      --pmc MfmaUtil MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE:
+      the share of SIMD cycles the matrix units were busy (MfmaUtil, the
+      busy cycles of all SIMDs over active cycles times SIMDs), the flops the
+      matrix units executed (bf16, and fp8 as MOPS x 512), and with --avg-us
+      the executed rate.
 """
 import argparse
 import csv
@@ -84,6 +92,26 @@ def traffic(args):
     print(json.dumps(rec))
 
 
+def mfma(args):
+    names = ["MfmaUtil", "MfmaFlopsBF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "GRBM_GUI_ACTIVE"]
+    rec = {"kernel": args.kernel}
+    for n in names:
+        v, cnt = _match(_per_kernel(args.csv, n), args.kernel)
+        rec[n] = v
+        rec["dispatches"] = cnt
+    flops = rec["MfmaFlopsBF16"] + rec["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
+    rec["executed_flops"] = flops
+    lines = [f"| quantity ({args.kernel}, mean of {rec['dispatches']} launches) | value |", "|---|---|",
+             f"| MfmaUtil (matrix-unit busy share of SIMD cycles) | {rec['MfmaUtil']:.1f}% |",
+             f"| executed MFMA flops, bf16 | {rec['MfmaFlopsBF16'] / 1e12:.4f} TFLOP |",
+             f"| executed MFMA flops, fp8 | {rec['SQ_INSTS_VALU_MFMA_MOPS_F8'] * 512 / 1e12:.4f} TFLOP |",
+             f"| GRBM_GUI_ACTIVE | {rec['GRBM_GUI_ACTIVE']:.0f} cycles |"]
+    if args.avg_us:
+        lines.append(f"| executed rate at {args.avg_us:.1f} us per launch | "
+                     f"{flops / (args.avg_us * 1e-6) / 1e12:.1f} TFLOP/s |")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     argv = list(sys.argv[1:] if argv is None else argv)
     if argv and argv[0].endswith(".db"):
@@ -98,9 +126,15 @@ def main(argv=None):
     f.add_argument("--kernel", required=True)
     f.add_argument("--workload", required=True)
     f.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--csv", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--avg-us", type=float, default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_table(a.db))
+    elif a.cmd == "mfma":
+        mfma(a)
     else:
         traffic(a)
 
