@@ -15,9 +15,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 
 // One row tile of one expert: rows [row0, row0 + nrows) of the expert-sorted
-// route order all belong to expert e.  ablk = row capacity / 32 (1, 2, 4 or
-// 8): an expert's segment is cut into full tiles of kTileRows rows and one
-// remainder tile of the smallest capacity (32, 64, 128 or 256) that holds it.
+// route order all belong to expert e.  ablk = row capacity / 32 (1, 2, 4, 6
+// or 8): an expert's segment is cut into full tiles of kTileRows rows and one
+// remainder tile of the smallest capacity (32, 64, 128, 192 or 256) that
+// holds it.  Kernels without a 192-row layout run class 6 as class 8.
 struct Tile {
   int e;
   int row0;

@@ -46,14 +46,19 @@ struct G8Ring {
 
 // Wave wv multiplies TT activation tiles by TW weight tiles (32 rows each).
 // An item has 4 weight tiles and AB activation tiles; with AB = 1 only waves
-// 0-3 have a pair (waves 4-7 still load).
+// 0-3 have a pair (waves 4-7 still load).  AB = 6 (192-row tiles): each wave
+// takes three activation tiles against one weight tile.
 template <int AB>
 struct G8Layout {
-  static constexpr int TT = AB >= 4 ? 2 : 1;
+  static constexpr int TT = AB == 6 ? 3 : AB >= 4 ? 2 : 1;
   static constexpr int TW = AB == 8 ? 2 : 1;
   __device__ static bool active(int wv) { return AB > 1 || wv < 4; }
   __device__ static int atile(int wv, int tt) {
-    return AB == 8 ? (wv >> 1) * 2 + tt : AB == 4 ? (wv >> 2) * 2 + tt : AB == 2 ? (wv >> 2) : 0;
+    return AB == 8   ? (wv >> 1) * 2 + tt
+           : AB == 6 ? (wv >> 2) * 3 + tt
+           : AB == 4 ? (wv >> 2) * 2 + tt
+           : AB == 2 ? (wv >> 2)
+                     : 0;
   }
   __device__ static int wtile(int wv, int tw) { return AB == 8 ? (wv & 1) * 2 + tw : (wv & 3); }
 };
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
     const Tile t = a.tiles[ti];
     switch (tile_class(t)) {
       case 8: g8_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
+      case 6: g8_item_any<GATEUP, 6>(a, t, n0, nb, ring, ring_lds); break;
       case 4: g8_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
       case 2: g8_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
       default: g8_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;

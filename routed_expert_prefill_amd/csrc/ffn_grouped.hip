@@ -81,7 +81,7 @@ __device__ int gs_scan(int v, int *total, int *buf) {
 }
 
 // One thread per expert: full 256-row tiles, then one remainder tile whose
-// height is the smallest of 32, 64, 128, 256 that holds it.  Tiles are
+// height is the smallest of 32, 64, 128, 192, 256 that holds it.  Tiles are
 // written tallest class first.
 __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     const int32_t *__restrict__ offsets, int E, Schedule *sch, Tile *__restrict__ tiles) {
@@ -94,12 +94,18 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
   }
   const int nfull = n / kTileRows;
   const int rem = n - nfull * kTileRows;
-  const int rab = rem == 0 ? 0 : rem <= 32 ? 1 : rem <= 64 ? 2 : rem <= 128 ? 4 : 8;
-  int cnt[4] = {nfull + (rab == 8), rab == 4, rab == 2, rab == 1};  // ablk 8, 4, 2, 1
-  int pos[4], tot[4];
-  for (int c = 0; c < 4; ++c) pos[c] = gs_scan(cnt[c], &tot[c], buf);
+  const int rab = rem == 0       ? 0
+                  : rem <= 32    ? 1
+                  : rem <= 64    ? 2
+                  : rem <= 128   ? 4
+                  : rem <= 192   ? 6
+                                 : 8;
+  constexpr int NC = 5;  // classes, tallest first: ablk 8, 6, 4, 2, 1
+  int cnt[NC] = {nfull + (rab == 8), rab == 6, rab == 4, rab == 2, rab == 1};
+  int pos[NC], tot[NC];
+  for (int c = 0; c < NC; ++c) pos[c] = gs_scan(cnt[c], &tot[c], buf);
   int base = 0;
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < NC; ++c) {
     pos[c] += base;
     base += tot[c];
   }
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     tiles[pos[0] + i] = t;
   }
   if (rab > 0 && rab < 8) {
-    const int c = rab == 4 ? 1 : rab == 2 ? 2 : 3;
+    const int c = rab == 6 ? 1 : rab == 4 ? 2 : rab == 2 ? 3 : 4;
     Tile t;
     t.e = e;
     t.row0 = row0 + nfull * kTileRows;
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     sch->n_tiles = base;
     sch->counter[0] = 0;
     sch->counter[1] = 0;
-    sch->n_small = tot[3];
+    sch->n_small = tot[NC - 1];
   }
 }
 
@@ -426,7 +432,8 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
       gg_item_any<GATEUP, 1, 64>(a, t, n0, nb, ring, ring_lds);
     } else {
       switch (tile_class(t)) {
-        case 8: gg_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
+        case 8:
+        case 6: gg_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
         case 4: gg_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
         case 2: gg_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
         default: gg_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;

@@ -6,8 +6,8 @@ fp8) at the same point, so what is left is fp32 accumulation order and rare
 bf16 rounding-boundary flips of h.
 
 The per-expert row counts below put experts in every tile capacity and at
-its edges: remainders of 1-32 rows (32-row tiles), 33-64, 65-128 and
-129-256, full 256-row tiles plus a remainder, and empty experts.
+its edges: remainders of 1-32 rows (32-row tiles), 33-64, 65-128, 129-192
+and 193-256, full 256-row tiles plus a remainder, and empty experts.
 """
 import numpy as np
 import pytest
@@ -81,7 +81,7 @@ def _check(got, ref, tol):
     return err, rel
 
 
-CLASS_COUNTS = [0, 1, 7, 16, 17, 31, 32, 33, 64, 128, 129, 160, 161, 300, 0, 2]
+CLASS_COUNTS = [0, 1, 7, 16, 17, 31, 32, 33, 64, 128, 129, 160, 161, 192, 193, 250, 300, 0, 2]
 
 
 @pytest.mark.parametrize("fp8", [False, True])
