@@ -17,6 +17,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -90,6 +91,18 @@ def traffic_from_profiles(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def device_facts():
+    """The GPU the run used and the published peaks the roofline fractions use."""
+    import torch
+
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1),
+            "peaks": {"hbm_gbs": HBM_PEAK_GBS, "mfma_tflops": MFMA_PEAK_TFLOPS,
+                      "at_clock_ghz": 2.4}}
+
+
 def cpu_baseline(wl, r, budget_s: float):
     """The fp64 oracle (expert-major, BLAS) on a bounded sample of the workload.
 
@@ -124,10 +137,20 @@ def cpu_baseline(wl, r, budget_s: float):
             done += chunk
     t_total = t_fixed + t_ffn / len(done) * len(active)
     blas = ",".join(sorted({str(i.get("internal_api")) for i in threadpool_info()}))
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(wl.T / t_total, 3),
         "unit": "tokens/s",
         "cores": cores,
+        "cpu": cpu_model,
         "kind": "oracle",
         "sample": (f"moe_ref_blocked (fp64 numpy, BLAS {blas}): route table and combine over all "
                    f"{wl.T} tokens plus the FFNs of {len(done)} of {len(active)} active experts "
@@ -316,6 +339,7 @@ def main():
         "roofline": roof,
         "router": router,
         "cpu_baseline": cpu,
+        "device": device_facts(),
         "kernel_source_sha": source_hash(),
     }
     _ = np
