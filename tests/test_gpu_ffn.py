@@ -151,10 +151,21 @@ def test_decode_sized_chunks(T, d, f, seed):
 
 SKINNY_COUNTS = [1, 5, 9, 17, 20, 24, 28, 31, 32, 3, 12, 7, 0, 30, 26, 15]
 MIXED_COUNTS = [40, 70, 130, 300, 10, 20, 5, 64, 200, 33, 1, 2, 0, 513]
+COUNT_SETS = {
+    "skinny": SKINNY_COUNTS,
+    "mixed": MIXED_COUNTS,
+    # 40 and 8 experts of at most 32 rows: at d = 2048 (eight blocks of 256
+    # outputs per tile) four-block items would leave fewer items than half
+    # the workgroups of a 256-CU device, so the kernel halves the blocks per
+    # item (to two for 40 experts, to one for 8)
+    "skinny40": [(7 * e) % 29 + 3 for e in range(40)],
+    "skinny8": [5, 32, 17, 1, 30, 9, 22, 14],
+}
 
 
 @pytest.mark.parametrize("fp8,counts,d", [
     (False, "skinny", 1024), (False, "mixed", 1024), (False, "skinny", 1536), (False, "mixed", 1536),
+    (False, "skinny40", 2048), (False, "skinny8", 2048),
     (True, "mixed", 384), (True, "mixed", 768), (True, "skinny", 1024)])
 def test_feature_blocks_per_item(fp8, counts, d):
     """Down-projection items of one, two and four feature blocks: only 32-row
@@ -163,7 +174,7 @@ def test_feature_blocks_per_item(fp8, counts, d):
     only by 512.  fp8 blocks are 128 outputs, each with its own row of weight
     block scales: d = 384 takes one block per item, 768 two, 1024 four.
     Every active row of y is written, every masked row is not."""
-    cnt = SKINNY_COUNTS if counts == "skinny" else MIXED_COUNTS
+    cnt = COUNT_SETS[counts]
     E, f = len(cnt), 256
     ids, mask = routing_with_counts(cnt, 6, seed=30, masked_extra=9)
     T, k = ids.shape
