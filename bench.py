@@ -18,6 +18,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -38,11 +39,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def _code_only(text: str) -> str:
+    """Kernel source without comments, trailing blanks and empty lines, so that
+    the hash changes with the code, not with its comments."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
+def source_hash(root: str = None) -> str:
+    """Hash of the grouped-GEMM kernel code (comments excluded)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root or ROOT, p), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,9 +9,10 @@
 // once: acc += s_w[n / 128][stage] * P.  The activation row scale is constant
 // along the reduction and multiplies the accumulator in the epilogue.  Items
 // carry 128 weight rows (gate/up: 64 features of both matrices, interleaved
-// in 16-row groups; down: 128 features), which keeps the fold of a wave in
-// proportion to its MFMAs.  Between the projections h is written in bf16 and
-// then quantised per row.
+// in 16-row groups; down: one to four blocks of 128 features streamed
+// through one ring fill), which keeps the fold of a wave in proportion to
+// its MFMAs; 192-row tiles have a layout of their own.  Between the
+// projections h is written in bf16 and then quantised per row.
 #include "kernels.h"
 #include "ring.h"
 

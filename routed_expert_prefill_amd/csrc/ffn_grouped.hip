@@ -8,15 +8,20 @@
 // schedule cuts each segment into row tiles whose height adapts to the rows
 // the expert received (adaptive MoE tiles and a persistent compact work
 // queue, "perf(ds4): unify gfx1151 sparse-prefill stack", Composition):
-// 256-row tiles, then one remainder tile of 32, 64, 128 or 256 rows.  The
-// tile list is ordered tallest class first and each workgroup repeatedly
-// takes the next item (tile, 128 or 256 output features) from an atomic
-// counter, so memory-bound items of small experts run on some compute units
-// while compute-bound items of large experts run on others.
+// 256-row tiles, then one remainder tile of 32, 64, 128, 192 or 256 rows
+// (192-row tiles use the 256-row layout here).  The tile list is ordered
+// tallest class first and each workgroup repeatedly takes the next item from
+// an atomic counter: a tile and 128 gate/up output features, or a tile and
+// one to four blocks of 256 down-projection features streamed through one
+// ring fill.  Memory-bound items of small experts run on some compute units
+// while compute-bound items of large experts run on others.  The weights of
+// an expert with a single tile are read once and go through non-temporal
+// loads.
 //
 // Every item streams both operands through the LDS stage ring (ring.h): 256
 // weight rows and 32 x ablk activation rows per 64-element reduction stage
-// (128-byte rows), with as many stages as the 160 KB of LDS holds (2 to 4).  MFMAs are 32x32x16
+// (128-byte rows), with as many stages as the 160 KB of LDS holds (2 to 4).
+// MFMAs are 32x32x16
 // bf16; eight waves (two per SIMD, so one wave's matrix work covers the
 // other's barrier and LDS waits) each own 32-row weight tiles:
 //   ablk = 8 (256 rows): wave w takes weight tiles 2(w%4), 2(w%4)+1 and the
