@@ -189,6 +189,41 @@ def test_feature_blocks_per_item(fp8, counts, d):
     assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
 
 
+def _random_case(seed):
+    """A seeded random shape: E, k, d, f, token count, mask rate and a skewed
+    (Zipf-like) expert choice, so that tiles of every class, skinny and mixed
+    queues and one-tile experts all occur across the seeds."""
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([8, 40, 100, 256]))
+    k = int(rng.choice([k for k in (1, 2, 6, 8) if k <= E]))
+    d = int(rng.choice([256, 512, 1024]))
+    f = int(rng.choice([128, 256, 384]))
+    T = int(rng.integers(1, 900 // k + 1))
+    p = (np.arange(1, E + 1, dtype=np.float64)) ** -float(rng.choice([0.0, 1.2, 2.0]))
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    mask = (rng.random((T, k)) >= float(rng.choice([0.0, 0.1, 0.5]))).astype(np.uint8)
+    w = rng.random((T, k)).astype(np.float32)
+    return E, k, d, f, ids, mask, w
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Random shapes against the per-token oracle, bf16 for even seeds and fp8
+    for odd ones; every active row of y written, no masked row."""
+    fp8 = seed % 2 == 1
+    E, k, d, f, ids, mask, w = _random_case(seed)
+    T = ids.shape[0]
+    x = _x(T, d, 40 + seed)
+    W = _weights(E, d, f, fp8, 50 + seed)
+    run, out = _run(ids, w, mask, x, W, E, fp8, y_fill=float("nan"))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+    n_act = int(run.rt.offsets[E].item())
+    y = run.y.cpu().numpy()
+    assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
+
+
 def test_single_expert_single_route_is_dense_mlp():
     """E = 1, k = 1, gate 1, no mask: a dense SwiGLU MLP, checked also against
     torch's own matmul on the GPU (an independent library product)."""
