@@ -41,8 +41,11 @@ struct Schedule {
   int n_tiles;     // entries of the tile list, tallest capacity first
   int counter[2];  // work-queue heads of the gate/up and down kernels
   int n_small;     // 32-row tiles, the last n_small entries of the list
-  int pad[60];     // keeps the tile list 256-byte aligned
+  int n_multi;     // tiles of experts with more than kTileRows rows, the first n_multi entries
+  int counter_s[2];  // second queue heads (items of the other tiles) of the two kernels
+  int pad[57];     // keeps the tile list 256-byte aligned
 };
+static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 256 bytes");
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
 // supplies row (l % 16) of its operand and the 8 consecutive reduction

@@ -10,13 +10,16 @@
 // queue, "perf(ds4): unify gfx1151 sparse-prefill stack", Composition):
 // 256-row tiles, then one remainder tile of 32, 64, 128, 192 or 256 rows
 // (192-row tiles use the 256-row layout here).  The tile list is ordered
-// tallest class first and each workgroup repeatedly takes the next item from
-// an atomic counter: a tile and 128 gate/up output features, or a tile and
+// tallest class first, the 256-row tiles of experts with several tiles ahead
+// of the rest, and each workgroup repeatedly takes the next item from one of
+// two atomic counters: a tile and 128 gate/up output features, or a tile and
 // one to four blocks of 256 down-projection features streamed through one
-// ring fill.  Memory-bound items of small experts run on some compute units
-// while compute-bound items of large experts run on others.  The weights of
-// an expert with a single tile are read once and go through non-temporal
-// loads.
+// ring fill.  One counter hands out the items of experts with several tiles
+// (compute-bound), the other those of single-tile experts (each a weight
+// stream); part of the workgroups start on each, so memory-bound items of
+// small experts run on some compute units while compute-bound items of large
+// experts run on others.  The weights of an expert with a single tile are
+// read once and go through non-temporal loads.
 //
 // Every item streams both operands through the LDS stage ring (ring.h): 256
 // weight rows and 32 x ablk activation rows per 64-element reduction stage
@@ -50,12 +53,18 @@ struct GgArgs {
   int nb;              // feature blocks per item (streamed through one ring fill)
   int nb_skinny;       // the same for 32-row tiles when nearly all tiles are 32-row ones
   const int *n_small;  // 32-row tiles at the end of the tile list
+  const int *n_multi;  // tiles of experts with several tiles, at the start of the list
+  int *counter_s;      // head of the second queue (items of the other tiles)
 };
 
 constexpr int kGgThreads = 512;
 constexpr int kGgWaves = kGgThreads / kWave;
 constexpr int kGgWRows = 256;
 constexpr int kGgRing = 160 * 1024;  // the whole LDS of a workgroup
+// cost of an item of an expert with several tiles, in quarters of an item of
+// a single-tile expert (sets the share of workgroups that start on the
+// weight streams)
+constexpr int kStreamShareWeight4 = 6;
 
 // Ring geometry of an item with 32 * AB activation rows: a stage is
 // (32 AB + 256) rows of 128 bytes, and the ring has as many slots as fit.
@@ -105,8 +114,12 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
                   : rem <= 128   ? 4
                   : rem <= 192   ? 6
                                  : 8;
-  constexpr int NC = 5;  // classes, tallest first: ablk 8, 6, 4, 2, 1
-  int cnt[NC] = {nfull + (rab == 8), rab == 6, rab == 4, rab == 2, rab == 1};
+  // classes, tallest first: ablk 8 of experts with several tiles, ablk 8 of
+  // single-tile experts, then 6, 4, 2, 1
+  constexpr int NC = 6;
+  const int n8 = nfull + (rab == 8);
+  const bool multi = n > kTileRows;
+  int cnt[NC] = {multi ? n8 : 0, multi ? 0 : n8, rab == 6, rab == 4, rab == 2, rab == 1};
   int pos[NC], tot[NC];
   for (int c = 0; c < NC; ++c) pos[c] = gs_scan(cnt[c], &tot[c], buf);
   int base = 0;
@@ -115,16 +128,16 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     base += tot[c];
   }
   const int stream = n <= kTileRows ? kTileStream : 0;  // the expert's only tile
-  for (int i = 0; i < cnt[0]; ++i) {
+  for (int i = 0; i < n8; ++i) {
     Tile t;
     t.e = e;
     t.row0 = row0 + i * kTileRows;
     t.nrows = min(kTileRows, n - i * kTileRows);
     t.ablk = 8 | stream;
-    tiles[pos[0] + i] = t;
+    tiles[pos[multi ? 0 : 1] + i] = t;
   }
   if (rab > 0 && rab < 8) {
-    const int c = rab == 6 ? 1 : rab == 4 ? 2 : rab == 2 ? 3 : 4;
+    const int c = rab == 6 ? 2 : rab == 4 ? 3 : rab == 2 ? 4 : 5;
     Tile t;
     t.e = e;
     t.row0 = row0 + nfull * kTileRows;
@@ -137,6 +150,9 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     sch->counter[0] = 0;
     sch->counter[1] = 0;
     sch->n_small = tot[NC - 1];
+    sch->n_multi = tot[0];
+    sch->counter_s[0] = 0;
+    sch->counter_s[1] = 0;
   }
 }
 
@@ -419,8 +435,46 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   const int items_big = nbig * ptb;
   const int items_mid = items_big + nsm * pts;
   const int total = items_mid + ntail * pt1;
+  // Two queues: the items of experts with several tiles (compute-bound,
+  // items [0, nc) of the order above) and those of all other tiles (each a
+  // stream of weights read once, [nc, total), tallest first).  The first
+  // ps workgroups start on the streams and the others on the compute items,
+  // each switching to the other queue when its own runs dry, so that the
+  // weight streams run beside the matrix work instead of after it; ps is
+  // the streams' share of the work, counting a compute item as
+  // kStreamShareWeight4 / 4 stream items, between 1/16 and 1/2 of the grid.
+  // MI355X, 8192 Zipf-routed tokens, against one queue: weights 1, 1.5, 2,
+  // 2.5 all helped gate/up (1.94-1.99 -> 1.86-1.91 ms), 1.5 was best for both
+  // kernels (down 1.12-1.14 -> 1.08 ms); 401 and 2048 tokens unchanged.
+  const int nc = *a.n_multi * ptb;
+  const int ns = total - nc;
+  const int G = gridDim.x;
+  const int ps = nc == 0 ? G
+                         : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
+                                                         (4LL * ns + (long long)kStreamShareWeight4 * nc))));
+  int src_q = (int)blockIdx.x < ps ? 1 : 0;  // 0: compute queue, 1: stream queue (thread 0)
   for (;;) {
-    if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
+    if (threadIdx.x == 0) {
+      int m = total;
+      for (int tries = 0; tries < 2; ++tries) {
+        if (src_q == 0) {
+          const int q = atomicAdd(a.counter, 1);
+          if (q < nc) {
+            m = q;
+            break;
+          }
+          src_q = 1;
+        } else {
+          const int q = atomicAdd(a.counter_s, 1);
+          if (q < ns) {
+            m = nc + q;
+            break;
+          }
+          src_q = 0;
+        }
+      }
+      *next_item = m;
+    }
     __syncthreads();
     // read before gg_item's first barrier (its loads overwrite it); uniform,
     // so the tile fetch below is a scalar load
@@ -518,6 +572,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
   g.tiles = L.tiles;
   g.ntiles = &L.sch->n_tiles;
   g.n_small = &L.sch->n_small;
+  g.n_multi = &L.sch->n_multi;
   if (stages & kStageGateUp) {
     g.act = L.x;
     g.sorted_routes = L.sorted_routes;
@@ -527,6 +582,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.N = L.f;
     g.K = L.d;
     g.counter = &L.sch->counter[0];
+    g.counter_s = &L.sch->counter_s[0];
     g.wr = item_weight_rows(L, L.f, 2);
     g.nb = 1;
     g.nb_skinny = 1;
@@ -541,6 +597,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.N = L.d;
     g.K = L.f;
     g.counter = &L.sch->counter[1];
+    g.counter_s = &L.sch->counter_s[1];
     g.wr = item_weight_rows(L, L.d, 1);
     g.nb = item_blocks(g.wr, L.d, 1, 2);
     g.nb_skinny = item_blocks(g.wr, L.d, 1, 4);

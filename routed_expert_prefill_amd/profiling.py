@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 output (kernel traces and counter runs).
 
-  python -m routed_expert_prefill_amd.profiling trace <run_results.db>
-      per-kernel table (calls, total, average, share) of a --kernel-trace run
+  python -m routed_expert_prefill_amd.profiling trace <run_results.db> [--skip N]
+      per-kernel table (calls, total, average, share) of a --kernel-trace run;
+      with --skip N also each kernel's average over its calls after the first N
   python -m routed_expert_prefill_amd.profiling traffic --fetch <csv> --write <csv>
           --kernel <name prefix> --workload <name> --out <json>
       HBM bytes per launch of one kernel from a FETCH_SIZE run and a
@@ -25,13 +26,29 @@ import sqlite3
 import sys
 
 
-def trace_table(db):
+def trace_table(db, skip=0):
+    """Per-kernel table; with skip > 0 also the average of each kernel's
+    calls after its first `skip` (the warm-up calls of the run)."""
     c = sqlite3.connect(db)
     rows = c.execute("select name, total_calls, total_duration, average, percentage "
                      "from top_kernels order by total_duration desc").fetchall()
-    out = ["| kernel | calls | total (us) | average (us) | share |", "|---|---|---|---|---|"]
+    steady = {}
+    if skip > 0:
+        per = {}
+        for name, dur in c.execute("select name, duration from kernels order by start"):
+            per.setdefault(name, []).append(dur / 1000.0)
+        steady = {n: sum(v[skip:]) / len(v[skip:]) for n, v in per.items() if len(v) > skip}
+    head = "| kernel | calls | total (us) | average (us) | share |"
+    rule = "|---|---|---|---|---|"
+    if skip > 0:
+        head += f" average after the first {skip} calls (us) |"
+        rule += "---|"
+    out = [head, rule]
     for name, calls, tot, avg, pct in rows:
-        out.append(f"| `{name.split('(')[0]}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.2f}% |")
+        line = f"| `{name.split('(')[0]}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.2f}% |"
+        if skip > 0:
+            line += f" {steady[name]:.2f} |" if name in steady else " — |"
+        out.append(line)
     return "\n".join(out)
 
 
@@ -120,6 +137,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("db")
+    t.add_argument("--skip", type=int, default=0,
+                   help="also average each kernel over its calls after the first SKIP")
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
@@ -132,7 +151,7 @@ def main(argv=None):
     m.add_argument("--avg-us", type=float, default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_table(a.db))
+        print(trace_table(a.db, a.skip))
     elif a.cmd == "mfma":
         mfma(a)
     else:
