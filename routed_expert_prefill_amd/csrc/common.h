@@ -47,6 +47,48 @@ struct Schedule {
 };
 static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 256 bytes");
 
+// Work dispatch of the persistent grouped-GEMM kernels from two queues:
+// items [0, nc) belong to experts with several 256-row tiles (compute-bound:
+// their weights serve every tile) and items [nc, total) to all other tiles
+// (each expert's weights read once: memory-bound streams, tallest first).
+// The first ps workgroups start on the streams and the others on the compute
+// items; each switches to the other queue when its own runs dry, so the
+// weight streams run beside the matrix work instead of after it.  ps is the
+// streams' share of the work, counting a compute item as 1.5 stream items
+// (kStreamShareWeight4 / 4), between 1/16 and 1/2 of the grid.  On MI355X,
+// 8192 Zipf-routed tokens (bf16), against one tallest-first queue: weights 1
+// to 2.5 all helped gate/up (1.94-1.99 -> 1.86-1.91 ms) and 1.5 was best for
+// both projections (down 1.12-1.14 -> 1.08 ms); 401 and 2048 tokens
+// unchanged.  Used by thread 0 of a workgroup only.
+constexpr int kStreamShareWeight4 = 6;
+
+struct TwoQueue {
+  int nc, ns, src;  // src: 0 = compute queue, 1 = stream queue
+  __device__ TwoQueue(int nc_, int total) : nc(nc_), ns(total - nc_) {
+    const int G = gridDim.x;
+    const int ps =
+        nc == 0 ? G
+                : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
+                                                (4LL * ns + (long long)kStreamShareWeight4 * nc))));
+    src = (int)blockIdx.x < ps ? 1 : 0;
+  }
+  // the next item, or nc + ns when both queues are empty
+  __device__ int next(int *compute_head, int *stream_head) {
+    for (int tries = 0; tries < 2; ++tries) {
+      if (src == 0) {
+        const int q = atomicAdd(compute_head, 1);
+        if (q < nc) return q;
+        src = 1;
+      } else {
+        const int q = atomicAdd(stream_head, 1);
+        if (q < ns) return nc + q;
+        src = 0;
+      }
+    }
+    return nc + ns;
+  }
+};
+
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
 // supplies row (l % 16) of its operand and the 8 consecutive reduction
 // indices 8*(l/16) .. 8*(l/16)+7; lane l receives D[4*(l/16) + r][l % 16],

@@ -2,7 +2,7 @@
 // fp32 scale per 128 x 128 block, E4M3 activations with one fp32 scale per
 // row (x per token, h per routed row).
 //
-// Same tile list, work queue and LDS stage ring as the bf16 kernels
+// Same tile list, two work queues and LDS stage ring as the bf16 kernels
 // (ffn_grouped.hip, ring.h).  A ring row is 128 bytes = 128 fp8 reduction
 // elements = one weight scale block, so each stage's partial product P (two
 // chained 32x32x64 fp8 MFMAs from zero) is folded into the fp32 accumulator
@@ -29,7 +29,9 @@ struct Gg8Args {
   int N, K;                // K <= 16384: a lane pair holds the K / 128 scales of a row
   const Tile *tiles;
   const int *ntiles;
-  int *counter;
+  const int *n_multi;  // tiles of experts with several tiles, at the start of the list
+  int *counter;        // compute-queue head (TwoQueue)
+  int *counter_s;      // stream-queue head
   int nb;  // feature blocks per item (streamed through one ring fill)
 };
 
@@ -372,8 +374,11 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
   const int FI = FEAT * nbi;  // output features per item
   const int per_tile = (a.N + FI - 1) / FI;
   const int total = ntiles * per_tile;
+  // two queues (TwoQueue): the items of the first n_multi tiles, whose
+  // experts have several tiles, and the rest
+  TwoQueue queue(*a.n_multi * per_tile, total);
   for (;;) {
-    if (threadIdx.x == 0) *next_item = atomicAdd(a.counter, 1);
+    if (threadIdx.x == 0) *next_item = queue.next(a.counter, a.counter_s);
     __syncthreads();
     // read before g8_item's first barrier (its loads overwrite it)
     const int it = __builtin_amdgcn_readfirstlane(*next_item);
@@ -407,6 +412,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
   g.k = L.k;
   g.tiles = L.tiles;
   g.ntiles = &L.sch->n_tiles;
+  g.n_multi = &L.sch->n_multi;
   if (stages & kStageGateUp) {
     g.act = L.qx;
     g.act_scale = L.sx;
@@ -419,6 +425,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.N = L.f;
     g.K = L.d;
     g.counter = &L.sch->counter[0];
+    g.counter_s = &L.sch->counter_s[0];
     g.nb = 1;
     hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
@@ -440,6 +447,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.N = L.d;
     g.K = L.f;
     g.counter = &L.sch->counter[1];
+    g.counter_s = &L.sch->counter_s[1];
     // the most blocks of 128 outputs, up to kG8MaxBlocks, that tile d
     // (MI355X, 8192 tokens: down 0.946 -> 0.877 ms with four, 0.884 with two)
     g.nb = kG8MaxBlocks;

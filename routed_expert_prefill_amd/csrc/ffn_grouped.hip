@@ -48,7 +48,7 @@ struct GgArgs {
   int N, K;
   const Tile *tiles;
   const int *ntiles;
-  int *counter;        // item queue head, zeroed by the schedule
+  int *counter;        // compute-queue head (TwoQueue), zeroed by the schedule
   int wr;              // weight rows per item: 256, or 128 / 64 when every tile holds <= 32 rows
   int nb;              // feature blocks per item (streamed through one ring fill)
   int nb_skinny;       // the same for 32-row tiles when nearly all tiles are 32-row ones
@@ -61,10 +61,6 @@ constexpr int kGgThreads = 512;
 constexpr int kGgWaves = kGgThreads / kWave;
 constexpr int kGgWRows = 256;
 constexpr int kGgRing = 160 * 1024;  // the whole LDS of a workgroup
-// cost of an item of an expert with several tiles, in quarters of an item of
-// a single-tile expert (sets the share of workgroups that start on the
-// weight streams)
-constexpr int kStreamShareWeight4 = 6;
 
 // Ring geometry of an item with 32 * AB activation rows: a stage is
 // (32 AB + 256) rows of 128 bytes, and the ring has as many slots as fit.
@@ -435,46 +431,11 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   const int items_big = nbig * ptb;
   const int items_mid = items_big + nsm * pts;
   const int total = items_mid + ntail * pt1;
-  // Two queues: the items of experts with several tiles (compute-bound,
-  // items [0, nc) of the order above) and those of all other tiles (each a
-  // stream of weights read once, [nc, total), tallest first).  The first
-  // ps workgroups start on the streams and the others on the compute items,
-  // each switching to the other queue when its own runs dry, so that the
-  // weight streams run beside the matrix work instead of after it; ps is
-  // the streams' share of the work, counting a compute item as
-  // kStreamShareWeight4 / 4 stream items, between 1/16 and 1/2 of the grid.
-  // MI355X, 8192 Zipf-routed tokens, against one queue: weights 1, 1.5, 2,
-  // 2.5 all helped gate/up (1.94-1.99 -> 1.86-1.91 ms), 1.5 was best for both
-  // kernels (down 1.12-1.14 -> 1.08 ms); 401 and 2048 tokens unchanged.
-  const int nc = *a.n_multi * ptb;
-  const int ns = total - nc;
-  const int G = gridDim.x;
-  const int ps = nc == 0 ? G
-                         : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
-                                                         (4LL * ns + (long long)kStreamShareWeight4 * nc))));
-  int src_q = (int)blockIdx.x < ps ? 1 : 0;  // 0: compute queue, 1: stream queue (thread 0)
+  // two queues (TwoQueue): the items of the first n_multi tiles, whose
+  // experts have several tiles, and the rest
+  TwoQueue queue(*a.n_multi * ptb, total);
   for (;;) {
-    if (threadIdx.x == 0) {
-      int m = total;
-      for (int tries = 0; tries < 2; ++tries) {
-        if (src_q == 0) {
-          const int q = atomicAdd(a.counter, 1);
-          if (q < nc) {
-            m = q;
-            break;
-          }
-          src_q = 1;
-        } else {
-          const int q = atomicAdd(a.counter_s, 1);
-          if (q < ns) {
-            m = nc + q;
-            break;
-          }
-          src_q = 0;
-        }
-      }
-      *next_item = m;
-    }
+    if (threadIdx.x == 0) *next_item = queue.next(a.counter, a.counter_s);
     __syncthreads();
     // read before gg_item's first barrier (its loads overwrite it); uniform,
     // so the tile fetch below is a scalar load
