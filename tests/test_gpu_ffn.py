@@ -111,6 +111,32 @@ def test_tile_classes(fp8):
     _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
 
 
+# Several experts with more than 256 rows (their 256-row tiles are handed out
+# from the compute queue) beside many small ones (the stream queue), so both
+# queues hold many items and workgroups switch between them.
+QUEUE_COUNTS = [700, 1, 520, 33, 257, 0, 300, 5, 64, 129, 17, 200, 2, 40, 90, 3, 513, 31, 8, 256]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_compute_and_stream_queues(fp8):
+    E = len(QUEUE_COUNTS)
+    d, f = 256, 256
+    ids, mask = routing_with_counts(QUEUE_COUNTS, 6, seed=11, masked_extra=29)
+    T, k = ids.shape
+    rng = np.random.default_rng(12)
+    w = rng.random((T, k)).astype(np.float32)
+    x = _x(T, d, 13)
+    W = _weights(E, d, f, fp8, 14)
+    run, out = _run(ids, w, mask, x, W, E, fp8, y_fill=float("nan"))
+    rt = route_table(ids, mask, E)
+    n_act = int(rt.offsets[E])
+    y = run.y.cpu().numpy()
+    assert not np.any(np.isnan(y[:n_act]))  # every item of both queues ran
+    assert np.all(np.isnan(y[n_act:]))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_tiny_workload_random_routing(fp8):
     rng = np.random.default_rng(5)
