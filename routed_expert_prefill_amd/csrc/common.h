@@ -54,22 +54,17 @@ static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 25
 // The first ps workgroups start on the streams and the others on the compute
 // items; each switches to the other queue when its own runs dry, so the
 // weight streams run beside the matrix work instead of after it.  ps is the
-// streams' share of the work, counting a compute item as 1.5 stream items
-// (kStreamShareWeight4 / 4), between 1/16 and 1/2 of the grid.  On MI355X,
-// 8192 Zipf-routed tokens (bf16), against one tallest-first queue: weights 1
-// to 2.5 all helped gate/up (1.94-1.99 -> 1.86-1.91 ms) and 1.5 was best for
-// both projections (down 1.12-1.14 -> 1.08 ms); 401 and 2048 tokens
-// unchanged.  Used by thread 0 of a workgroup only.
-constexpr int kStreamShareWeight4 = 6;
-
+// streams' share of the work, counting a compute item as weight4 / 4 stream
+// items, between 1/16 and 1/2 of the grid.  Used by thread 0 of a workgroup
+// only.
 struct TwoQueue {
   int nc, ns, src;  // src: 0 = compute queue, 1 = stream queue
-  __device__ TwoQueue(int nc_, int total) : nc(nc_), ns(total - nc_) {
+  __device__ TwoQueue(int nc_, int total, int weight4) : nc(nc_), ns(total - nc_) {
     const int G = gridDim.x;
     const int ps =
         nc == 0 ? G
                 : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
-                                                (4LL * ns + (long long)kStreamShareWeight4 * nc))));
+                                                (4LL * ns + (long long)weight4 * nc))));
     src = (int)blockIdx.x < ps ? 1 : 0;
   }
   // the next item, or nc + ns when both queues are empty

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
   const int total = ntiles * per_tile;
   // two queues (TwoQueue): the items of the first n_multi tiles, whose
   // experts have several tiles, and the rest
-  TwoQueue queue(*a.n_multi * per_tile, total);
+  TwoQueue queue(*a.n_multi * per_tile, total, GATEUP ? 6 : 9);  // the bf16 kernels' weights
   for (;;) {
     if (threadIdx.x == 0) *next_item = queue.next(a.counter, a.counter_s);
     __syncthreads();
