@@ -86,7 +86,7 @@ typedef struct moe_ffn_desc {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *moe_status_string(int status);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2. */
 int moe_abi_version(void);
 
 /* ------------------------------------------------------------ route build
@@ -111,7 +111,7 @@ int moe_abi_version(void);
  * workspace   device scratch of at least moe_route_build_workspace(T,k,E)
  *             bytes; contents on entry are ignored.
  * Errors: MOE_EINVAL (null output, T < 1, k < 1, T*k >= 2^31),
- *         MOE_EUNSUPPORTED (E < 1 or E > 256, k > 16), MOE_EALIGN,
+ *         MOE_EUNSUPPORTED (E < 1 or E > 256, k > 16 or k > E), MOE_EALIGN,
  *         MOE_EWORKSPACE.
  */
 size_t moe_route_build_workspace(int T, int k, int E);
@@ -185,44 +185,54 @@ int moe_ffn_down(const moe_ffn_desc *desc /* host */, const int32_t *offsets, co
  * gfx1151 A/B; "perf(ds4): extend sparse prefill scheduling to 10K",
  * Historical fused-combine discriminator):
  *
- *   out[t] = sum over j = 0..k-1 ascending, route active, of
+ *   out[t] = sum over j = 0..k-1 ascending, route read, of
  *            topk_w[t,j] * y[route_rows[t*k+j]]          (fp32, from +0.0)
  *
- * A masked route is never read -- its gate, its route_rows entry and its row
- * of y may hold anything, NaN included -- so it contributes an exact zero
- * ("perf(ds4): batch heterogeneous MoE prefill by expert", Summary and
- * Correctness and validation).  A token with no active route gets +0.0.
- * A route whose id is outside [0,E) counts as masked only through
- * moe_route_build; here route_mask alone decides.
+ * Route r is read when route_mask[r] != 0 (or route_mask is NULL) and, if
+ * row_limit is given, route_rows[r] < *row_limit.  A route that is not read
+ * -- its gate, its route_rows entry and its row of y may hold anything, NaN
+ * included -- contributes an exact zero ("perf(ds4): batch heterogeneous MoE
+ * prefill by expert", Summary and Correctness and validation).  A token with
+ * no route read gets +0.0.
  *
- * y           fp32 [rows, d] with route_rows[r] < rows for every active r
+ * row_limit is the bound that makes the combine agree with moe_route_build:
+ * pass offsets + E (device pointer to offsets[E], the number of rows of y
+ * moe_grouped_ffn writes).  moe_route_build sends masked routes AND active
+ * routes whose id lies outside [0,E) to rows at or past offsets[E], which the
+ * FFN never writes, so with the bound such routes are skipped like masked
+ * ones.  With row_limit NULL, route_mask alone decides.
+ *
+ * y           fp32 [rows, d] with route_rows[r] < rows for every route read
  * route_rows  int32 [T*k]; topk_w fp32 [T,k]; route_mask uint8 [T,k] or NULL
+ * row_limit   int32 [1] or NULL (4-byte aligned; read once by the kernel)
  * out         fp32 [T,d]
  * Errors: MOE_EINVAL (null, T < 1, k < 1, d < 4 or d not a multiple of 4),
  *         MOE_EUNSUPPORTED (k > 16), MOE_EALIGN, MOE_EHIP.
  */
 int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
-                const uint8_t *route_mask, int T, int k, int d, float *out,
-                moe_stream_t stream);
+                const uint8_t *route_mask, const int32_t *row_limit, int T, int k, int d,
+                float *out, moe_stream_t stream);
 
 /* ------------------------------------------------------------ combine, shared-output form
  * The combine writing into the layer's shared-expert output (the fused
  * combine's "shared-output" cases, "perf(ds4): extend sparse prefill
  * scheduling to 10K", Historical fused-combine discriminator):
  *
- *   routed[t]   = the moe_combine sum (fp32, ascending j from +0.0, masked routes never read)
+ *   routed[t]   = the moe_combine sum (fp32, ascending j from +0.0, routes
+ *                 not read contribute nothing)
  *   out[t]      = routed[t] + shared[t]   (one fp32 addition; out = routed if shared is NULL)
  *   out_bf16[t] = bf16 round-to-nearest-even of out[t]
  *
  * shared fp32 [T,d] or NULL; out fp32 [T,d] or NULL; out_bf16 bf16 [T,d] or
- * NULL (at least one of out, out_bf16).  Other arguments as for moe_combine.
+ * NULL (at least one of out, out_bf16).  Other arguments, row_limit
+ * included, as for moe_combine.
  * Errors: MOE_EINVAL (null y/route_rows/topk_w, both outputs null, T < 1,
  *         k < 1, d < 4 or d not a multiple of 4), MOE_EUNSUPPORTED (k > 16),
  *         MOE_EALIGN, MOE_EHIP.
  */
 int moe_combine_shared(const float *y, const int32_t *route_rows, const float *topk_w,
-                       const uint8_t *route_mask, const float *shared, int T, int k, int d,
-                       float *out, void *out_bf16, moe_stream_t stream);
+                       const uint8_t *route_mask, const int32_t *row_limit, const float *shared,
+                       int T, int k, int d, float *out, void *out_bf16, moe_stream_t stream);
 
 /* ------------------------------------------------------------ router
  * Top-k expert selection and gates from router logits, the step ahead of

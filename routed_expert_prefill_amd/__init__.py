@@ -185,8 +185,23 @@ def ffn_down(desc: MoeFfnDesc, offsets, w_down, s_down, y, workspace):
     _lib.check(rc, "moe_ffn_down")
 
 
-def combine(y, route_rows, topk_w, route_mask, out=None):
-    """moe_combine: out[t] = sum over active j of w[t,j] * y[route_rows[t*k+j]] (fp32)."""
+def _row_limit(row_limit):
+    """The combine's row bound: a one-element int32 device tensor (for
+    instance ``offsets[E:E + 1]`` of a route table) or None."""
+    torch = _torch()
+    if row_limit is None:
+        return None
+    if not isinstance(row_limit, torch.Tensor) or row_limit.dtype != torch.int32 or \
+            row_limit.numel() != 1 or row_limit.device.type != "cuda":
+        raise TypeError("row_limit must be a one-element int32 GPU tensor")
+    return row_limit.data_ptr()
+
+
+def combine(y, route_rows, topk_w, route_mask, out=None, row_limit=None):
+    """moe_combine: out[t] = sum over read j of w[t,j] * y[route_rows[t*k+j]] (fp32).
+
+    Route r is read when its mask is set and, with row_limit (offsets[E:E+1]
+    of the route table), its row lies below offsets[E]."""
     torch = _torch()
     lib = _lib.load()
     _need(y, "y", torch.float32, 2)
@@ -194,19 +209,20 @@ def combine(y, route_rows, topk_w, route_mask, out=None):
     _need(topk_w, "topk_w", torch.float32, 2)
     if route_mask is not None:
         _need(route_mask, "route_mask", torch.uint8, 2)
+    lim = _row_limit(row_limit)
     T, k = topk_w.shape
     d = y.shape[1]
     if out is None:
         out = torch.empty(T, d, dtype=torch.float32, device=y.device)
     _need(out, "out", torch.float32, 2)
-    rc = lib.moe_combine(_ptr(y), _ptr(route_rows), _ptr(topk_w), _ptr(route_mask), T, k, d,
-                         _ptr(out), _stream())
+    rc = lib.moe_combine(_ptr(y), _ptr(route_rows), _ptr(topk_w), _ptr(route_mask), lim, T, k,
+                         d, _ptr(out), _stream())
     _lib.check(rc, "moe_combine")
     return out
 
 
 def combine_shared(y, route_rows, topk_w, route_mask, shared=None, out=None, out_bf16=None,
-                   want_fp32=True, want_bf16=False):
+                   want_fp32=True, want_bf16=False, row_limit=None):
     """moe_combine_shared: routed combine plus the shared-expert rows, as fp32
     and/or bf16 (round to nearest even)."""
     torch = _torch()
@@ -216,6 +232,7 @@ def combine_shared(y, route_rows, topk_w, route_mask, shared=None, out=None, out
     _need(topk_w, "topk_w", torch.float32, 2)
     if route_mask is not None:
         _need(route_mask, "route_mask", torch.uint8, 2)
+    lim = _row_limit(row_limit)
     T, k = topk_w.shape
     d = y.shape[1]
     if shared is not None:
@@ -230,7 +247,7 @@ def combine_shared(y, route_rows, topk_w, route_mask, shared=None, out=None, out
         _need(out, "out", torch.float32, 2)
     if out_bf16 is not None:
         _need(out_bf16, "out_bf16", torch.bfloat16, 2)
-    rc = lib.moe_combine_shared(_ptr(y), _ptr(route_rows), _ptr(topk_w), _ptr(route_mask),
+    rc = lib.moe_combine_shared(_ptr(y), _ptr(route_rows), _ptr(topk_w), _ptr(route_mask), lim,
                                 _ptr(shared), T, k, d, _ptr(out), _ptr(out_bf16), _stream())
     _lib.check(rc, "moe_combine_shared")
     return out, out_bf16
@@ -273,6 +290,11 @@ class MoEPrefill:
         self.ffn_ws = _ffn_ws(self.desc, dev, None)
         self.y = torch.empty(R, d, dtype=torch.float32, device=dev)
         self.out = torch.empty(T, d, dtype=torch.float32, device=dev)
+        # offsets[E]: rows of y the FFN writes.  The combine reads no route at
+        # or past it, so active routes whose ids lie outside [0, E) -- which
+        # the route build sends to the trailing bin -- add exact zeros, as
+        # masked ones do.
+        self.row_limit = self.rt.offsets[E:E + 1]
 
     def __call__(self, x, topk_ids, topk_w, route_mask, w_gate, w_up, w_down, s_gate=None,
                  s_up=None, s_down=None, stage_events=None):
@@ -289,7 +311,8 @@ class MoEPrefill:
         if ev is None:
             grouped_ffn(x, rt.offsets, rt.sorted_routes, w_gate, w_up, w_down, self.k, s_gate,
                         s_up, s_down, y=self.y, workspace=self.ffn_ws)
-            return combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out)
+            return combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out,
+                           row_limit=self.row_limit)
         def mark(i):
             if ev[i] is not None:
                 ev[i].record()
@@ -301,6 +324,7 @@ class MoEPrefill:
         mark(3)
         ffn_down(self.desc, rt.offsets, w_down, s_down, self.y, self.ffn_ws)
         mark(4)
-        out = combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out)
+        out = combine(self.y, rt.route_rows, topk_w, route_mask, out=self.out,
+                      row_limit=self.row_limit)
         mark(5)
         return out

@@ -4,7 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_prefill.so")
+# MOE_PREFILL_LIB names another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree gfx950 build.
+LIB_PATH = os.environ.get("MOE_PREFILL_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_prefill.so")
 
 MOE_OK = 0
 MOE_EINVAL = -1
@@ -72,11 +75,11 @@ def load() -> ctypes.CDLL:
     lib.moe_ffn_down.restype = i32
     lib.moe_ffn_down.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine.restype = i32
-    lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.moe_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_quant_rows_fp8.restype = i32
     lib.moe_quant_rows_fp8.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_combine_shared.restype = i32
-    lib.moe_combine_shared.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_combine_shared.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.moe_route_topk.restype = i32
     lib.moe_route_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     _lib = lib

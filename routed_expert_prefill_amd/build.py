@@ -69,6 +69,66 @@ def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BU
     return out
 
 
+# Host-side sanitizers for the C ABI layer only: AddressSanitizer and
+# UndefinedBehaviorSanitizer apply to the host pass of api.cpp (each flag
+# behind -Xarch_host, so no GPU code is instrumented); the kernels are the
+# normal gfx950 objects.  The result is loaded with the clang ASan runtime
+# preloaded (sanitizer_runtime()) by the CPU tests of the ABI.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                 "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime():
+    """Path of the clang ASan runtime shared library of the ROCm toolchain, or None."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized(out_dir: str = os.path.join(BUILD, "host_sanitized")) -> str:
+    """libmoe_prefill.so with the host code of api.cpp built under ASan and
+    UBSan; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        _run([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    api = os.path.join(out_dir, "api.cpp.o")
+    _run([cc, *[f for f in COMMON if f != "-O3"], "-O1", "-g", *DEVICE, *HOST_SANITIZE, "-x", "hip",
+          "-c", os.path.join(CSRC, "api.cpp"), "-o", api])
+    lib = os.path.join(out_dir, "libmoe_prefill.so")
+    _run([cc, "-shared", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib, api, *objs])
+    return lib
+
+
+def kernel_resource_report(src: str) -> dict:
+    """Per-kernel resource usage of one HIP source compiled for gfx950, from
+    the compiler's kernel-resource-usage remarks: {kernel: {field: value}}."""
+    import re
+
+    cmd = [hipcc(), *COMMON, *DEVICE, "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage",
+           "-c", os.path.join(CSRC, src), "-o", os.devnull]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("build failed: " + " ".join(cmd) + "\n" + p.stdout)
+    out, cur = {}, None
+    for line in p.stdout.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+) \[-Rpass", line)
+        if m and cur is not None:
+            out[cur][m.group(1).strip()] = int(m.group(2))
+    return out
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

@@ -17,6 +17,10 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Scalars read once by a kernel (the combine's row limit) need only their
+// own alignment.
+bool misaligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+
 int status_from(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 int num_cus_current_device() {
@@ -112,7 +116,7 @@ const char *moe_status_string(int status) {
   }
 }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 size_t moe_route_build_workspace(int T, int k, int E) {
   if (T < 1 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS || (long long)T * k >= (1LL << 31)) return 0;
@@ -125,7 +129,7 @@ int moe_route_build(const int32_t *topk_ids, const uint8_t *route_mask, int T, i
                     moe_stream_t stream) {
   if (!topk_ids || !counts || !offsets || !sorted_routes || !route_rows) return MOE_EINVAL;
   if (T < 1 || k < 1 || (long long)T * k >= (1LL << 31)) return MOE_EINVAL;
-  if (E < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+  if (E < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_EUNSUPPORTED;
   if (misaligned(topk_ids) || misaligned(counts) || misaligned(offsets) ||
       misaligned(sorted_routes) || misaligned(route_rows) || misaligned(workspace) ||
       (route_mask && misaligned(route_mask)))
@@ -257,29 +261,30 @@ int moe_ffn_down(const moe_ffn_desc *desc, const int32_t *offsets, const void *w
 }
 
 int moe_combine(const float *y, const int32_t *route_rows, const float *topk_w,
-                const uint8_t *route_mask, int T, int k, int d, float *out,
-                moe_stream_t stream) {
+                const uint8_t *route_mask, const int32_t *row_limit, int T, int k, int d,
+                float *out, moe_stream_t stream) {
   if (!y || !route_rows || !topk_w || !out) return MOE_EINVAL;
   if (T < 1 || k < 1 || d < 4 || d % 4 != 0 || (long long)T * k >= (1LL << 31)) return MOE_EINVAL;
   if (k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
   if (misaligned(y) || misaligned(route_rows) || misaligned(topk_w) || misaligned(out) ||
-      (route_mask && misaligned(route_mask)))
+      (route_mask && misaligned(route_mask)) || (row_limit && misaligned4(row_limit)))
     return MOE_EALIGN;
-  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, nullptr, T, k, d, out,
-                                         nullptr, static_cast<hipStream_t>(stream)));
+  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, row_limit, nullptr, T,
+                                         k, d, out, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine_shared(const float *y, const int32_t *route_rows, const float *topk_w,
-                       const uint8_t *route_mask, const float *shared, int T, int k, int d,
-                       float *out, void *out_bf16, moe_stream_t stream) {
+                       const uint8_t *route_mask, const int32_t *row_limit, const float *shared,
+                       int T, int k, int d, float *out, void *out_bf16, moe_stream_t stream) {
   if (!y || !route_rows || !topk_w || (!out && !out_bf16)) return MOE_EINVAL;
   if (T < 1 || k < 1 || d < 4 || d % 4 != 0 || (long long)T * k >= (1LL << 31)) return MOE_EINVAL;
   if (k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
   const void *ptrs[] = {y, route_rows, topk_w, route_mask, shared, out, out_bf16};
   for (const void *p : ptrs)
     if (p && misaligned(p)) return MOE_EALIGN;
-  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, shared, T, k, d, out,
-                                         static_cast<uint16_t *>(out_bf16),
+  if (row_limit && misaligned4(row_limit)) return MOE_EALIGN;
+  return status_from(moe::launch_combine(y, route_rows, topk_w, route_mask, row_limit, shared, T,
+                                         k, d, out, static_cast<uint16_t *>(out_bf16),
                                          static_cast<hipStream_t>(stream)));
 }
 

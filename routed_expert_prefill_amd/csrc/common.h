@@ -14,6 +14,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
+// v as an opaque vector-register value.  Loop-invariant bookkeeping of the
+// persistent kernels (work dispatch) is built from such values: the
+// compiler can then neither keep it nor anything it hoists from it in the
+// scalar registers, which the inner loops need, and there is room for it in
+// the vector registers.
+__device__ __forceinline__ int vreg(int v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // One row tile of one expert: rows [row0, row0 + nrows) of the expert-sorted
 // route order all belong to expert e.  ablk = row capacity / 32 (1, 2, 4, 6
 // or 8): an expert's segment is cut into full tiles of kTileRows rows and one
@@ -43,7 +53,8 @@ struct Schedule {
   int n_small;     // 32-row tiles, the last n_small entries of the list
   int n_multi;     // tiles of experts with more than kTileRows rows, the first n_multi entries
   int counter_s[2];  // second queue heads (items of the other tiles) of the two kernels
-  int pad[57];     // keeps the tile list 256-byte aligned
+  int done[2];     // workgroups of the gate/up and down kernels that have left their queues
+  int pad[55];     // keeps the tile list 256-byte aligned
 };
 static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 256 bytes");
 
@@ -56,19 +67,20 @@ static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 25
 // weight streams run beside the matrix work instead of after it.  ps is the
 // streams' share of the work, counting a compute item as weight4 / 4 stream
 // items, between 1/16 and 1/2 of the grid.  Used by thread 0 of a workgroup
-// only.
+// only.  Both members are forced inline: as calls they kept the object in
+// the private segment (scratch memory) and made the caller save registers.
 struct TwoQueue {
   int nc, ns, src;  // src: 0 = compute queue, 1 = stream queue
-  __device__ TwoQueue(int nc_, int total, int weight4) : nc(nc_), ns(total - nc_) {
-    const int G = gridDim.x;
+  __device__ __forceinline__ TwoQueue(int nc_, int total, int weight4, int G)
+      : nc(nc_), ns(total - nc_) {
     const int ps =
         nc == 0 ? G
                 : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
                                                 (4LL * ns + (long long)weight4 * nc))));
-    src = (int)blockIdx.x < ps ? 1 : 0;
+    src = vreg((int)blockIdx.x) < ps ? 1 : 0;
   }
   // the next item, or nc + ns when both queues are empty
-  __device__ int next(int *compute_head, int *stream_head) {
+  __device__ __forceinline__ int next(int *compute_head, int *stream_head) {
     for (int tries = 0; tries < 2; ++tries) {
       if (src == 0) {
         const int q = atomicAdd(compute_head, 1);
@@ -83,6 +95,21 @@ struct TwoQueue {
     return nc + ns;
   }
 };
+
+// Called by thread 0 of each workgroup of a persistent GEMM after its last
+// queue access.  The last workgroup of the grid to arrive resets the
+// kernel's two queue heads and the arrival count, so the same stage can run
+// again on the same schedule.  The fence orders this workgroup's queue
+// atomics before its arrival; the last arrival therefore follows every
+// queue access of the grid.
+__device__ __forceinline__ void queue_release(int *compute_head, int *stream_head, int *done) {
+  __threadfence();
+  if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
+    atomicExch(compute_head, 0);
+    atomicExch(stream_head, 0);
+    atomicExch(done, 0);
+  }
+}
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
 // supplies row (l % 16) of its operand and the 8 consecutive reduction

@@ -32,6 +32,7 @@ struct Gg8Args {
   const int *n_multi;  // tiles of experts with several tiles, at the start of the list
   int *counter;        // compute-queue head (TwoQueue)
   int *counter_s;      // stream-queue head
+  int *done;           // workgroups that have left the queues (queue_release)
   int nb;  // feature blocks per item (streamed through one ring fill)
 };
 
@@ -361,41 +362,65 @@ __device__ __forceinline__ void g8_item_any(const Gg8Args &a, const Tile &t, int
 template <bool GATEUP>
 __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kG8Ring];
-  // the queue head is passed through the idle ring between items
+  // the next item (tile index, first feature, blocks, reduction length; tile
+  // -1 = none left) is passed from thread 0 through the idle ring between
+  // items
   int *next_item = reinterpret_cast<int *>(ring);
   const uint32_t ring_lds = lds_addr(ring);
   constexpr int FEAT = GATEUP ? 64 : 128;  // output features per block
+  // The dispatch state is built from vreg() values (common.h): it stays in
+  // vector registers and nothing derived from it is hoisted into the scalar
+  // registers the item loop needs.
   // blocks per item: halved while fewer than half the workgroups would get
   // an item (counts above one divide the feature blocks of a tile)
-  const int ntiles = *a.ntiles;
-  const int pt1 = (a.N + FEAT - 1) / FEAT;
-  int nbi = a.nb;
-  while (nbi > 1 && 2 * ntiles * (pt1 / nbi) < (int)gridDim.x) nbi >>= 1;
+  const int N = vreg(a.N), grid = vreg((int)gridDim.x);
+  const int ntiles = vreg(*a.ntiles);
+  const int pt1 = (N + FEAT - 1) / FEAT;
+  int nbi = vreg(a.nb);
+  while (nbi > 1 && 2 * ntiles * (pt1 / nbi) < grid) nbi >>= 1;
   const int FI = FEAT * nbi;  // output features per item
-  const int per_tile = (a.N + FI - 1) / FI;
+  const int per_tile = (N + FI - 1) / FI;
   const int total = ntiles * per_tile;
   // two queues (TwoQueue): the items of the first n_multi tiles, whose
-  // experts have several tiles, and the rest
-  TwoQueue queue(*a.n_multi * per_tile, total, GATEUP ? 6 : 9);  // the bf16 kernels' weights
+  // experts have several tiles, and the rest (a compute item weighed as in
+  // the bf16 kernels)
+  TwoQueue queue(vreg(*a.n_multi) * per_tile, total, GATEUP ? 6 : 9, grid);
   for (;;) {
-    if (threadIdx.x == 0) *next_item = queue.next(a.counter, a.counter_s);
+    if (threadIdx.x == 0) {
+      const int it = queue.next(a.counter, a.counter_s);
+      int ti = -1, n0 = 0, nb = 0;
+      if (it < total) {
+        ti = it / per_tile;
+        n0 = (it - ti * per_tile) * FI;
+        nb = min(nbi, (N - n0 + FEAT - 1) / FEAT);
+      } else {
+        queue_release(a.counter, a.counter_s, a.done);
+      }
+      next_item[0] = ti;
+      next_item[1] = n0;
+      next_item[2] = nb;
+      next_item[3] = a.K;
+    }
     __syncthreads();
-    // read before g8_item's first barrier (its loads overwrite it)
-    const int it = __builtin_amdgcn_readfirstlane(*next_item);
-    if (it >= total) break;
-    const int ti = it / per_tile;
-    const int n0 = (it - ti * per_tile) * FI;
-    const int nb = min(nbi, (a.N - n0 + FEAT - 1) / FEAT);
+    // read before g8_item's first barrier (its loads overwrite it); the
+    // reduction length comes through LDS so that nothing derived from it is
+    // hoisted out of the loop into the scalar registers
+    const int ti = __builtin_amdgcn_readfirstlane(next_item[0]);
+    if (ti < 0) break;
+    const int n0 = __builtin_amdgcn_readfirstlane(next_item[1]);
+    const int nb = __builtin_amdgcn_readfirstlane(next_item[2]);
+    Gg8Args ai = a;
+    ai.K = __builtin_amdgcn_readfirstlane(next_item[3]);
     const Tile t = a.tiles[ti];
     switch (tile_class(t)) {
-      case 8: g8_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
-      case 6: g8_item_any<GATEUP, 6>(a, t, n0, nb, ring, ring_lds); break;
-      case 4: g8_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
-      case 2: g8_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
-      default: g8_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;
+      case 8: g8_item_any<GATEUP, 8>(ai, t, n0, nb, ring, ring_lds); break;
+      case 6: g8_item_any<GATEUP, 6>(ai, t, n0, nb, ring, ring_lds); break;
+      case 4: g8_item_any<GATEUP, 4>(ai, t, n0, nb, ring, ring_lds); break;
+      case 2: g8_item_any<GATEUP, 2>(ai, t, n0, nb, ring, ring_lds); break;
+      default: g8_item_any<GATEUP, 1>(ai, t, n0, nb, ring, ring_lds); break;
     }
-    // the ring (and the queue head in it) is rewritten only after every wave
-    // has passed this barrier
+    // the ring (and the item in it) is rewritten only after every wave has
+    // passed this barrier
     __syncthreads();
   }
 }
@@ -426,6 +451,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.K = L.d;
     g.counter = &L.sch->counter[0];
     g.counter_s = &L.sch->counter_s[0];
+    g.done = &L.sch->done[0];
     g.nb = 1;
     hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
@@ -448,6 +474,7 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.K = L.f;
     g.counter = &L.sch->counter[1];
     g.counter_s = &L.sch->counter_s[1];
+    g.done = &L.sch->done[1];
     // the most blocks of 128 outputs, up to kG8MaxBlocks, that tile d
     // (MI355X, 8192 tokens: down 0.946 -> 0.877 ms with four, 0.884 with two)
     g.nb = kG8MaxBlocks;

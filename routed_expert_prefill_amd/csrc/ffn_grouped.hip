@@ -62,6 +62,7 @@ struct GgArgs {
   const int *n_small;  // 32-row tiles at the end of the tile list
   const int *n_multi;  // tiles of experts with several tiles, at the start of the list
   int *counter_s;      // head of the second queue (items of the other tiles)
+  int *done;           // workgroups that have left the queues (queue_release)
 };
 
 constexpr int kGgThreads = 512;
@@ -156,6 +157,8 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     sch->n_multi = tot[0];
     sch->counter_s[0] = 0;
     sch->counter_s[1] = 0;
+    sch->done[0] = 0;
+    sch->done[1] = 0;
   }
 }
 
@@ -395,49 +398,88 @@ __device__ __forceinline__ void gg_item_any(const GgArgs &a, const Tile &t, int 
 
 // ------------------------------------------------------------------ kernel
 
+// The item order and shape of the bf16 persistent kernels: which tile and
+// which output features item `it` covers.  Its state lives in vector
+// registers (there is room there; the inputs go through vreg()), so that the
+// compiler neither holds it nor values hoisted from it in the scalar
+// registers while the workgroup multiplies, and only thread 0 decodes items.
+template <bool GATEUP>
+struct GgDispatch {
+  int nbig, nsm, ptb, pts, pt1, FEAT, FIB, FIS, nbb, nbs, items_big, items_mid, total, N, grid;
+  __device__ __forceinline__ explicit GgDispatch(const GgArgs &a) {
+    N = vreg(a.N);
+    grid = vreg((int)gridDim.x);
+    const int wr = vreg(a.wr);
+    // output features per item: half the weight rows for gate/up (gate and up
+    // rows of the same features), all of them for down
+    FEAT = GATEUP ? wr / 2 : wr;
+    // items of taller tiles first (the list is tallest first), then of the
+    // 32-row tiles; the 32-row tiles take nb_skinny blocks per item when the
+    // taller ones are at most an eighth as many (on MI355X, 4 blocks were
+    // best there and 2 elsewhere, for 200 to 8192 tokens)
+    const int nsmall = vreg(*a.n_small);
+    nbig = vreg(*a.ntiles) - nsmall;
+    const bool skinny = nbig * 8 <= nsmall;
+    nbb = vreg(a.nb);
+    nbs = skinny ? vreg(a.nb_skinny) : nbb;
+    // with few tiles, halve the blocks per item until at least half the
+    // workgroups have an item: a workgroup of a half-idle chip streams faster
+    // than its even share, so long items on half of them still pay (measured:
+    // 11 experts 0.175 -> 0.123 ms with the halving, 43 experts 4% slower if
+    // every workgroup had to get one).  Block counts above one divide the
+    // feature blocks of a tile.
+    pt1 = (N + FEAT - 1) / FEAT;
+    while ((nbb > 1 || nbs > 1) && 2 * (nbig * (pt1 / nbb) + nsmall * (pt1 / nbs)) < grid) {
+      if (nbs >= nbb)
+        nbs >>= 1;
+      else
+        nbb >>= 1;
+    }
+    FIB = FEAT * nbb;  // output features per item
+    FIS = FEAT * nbs;
+    ptb = (N + FIB - 1) / FIB;
+    pts = (N + FIS - 1) / FIS;
+    // when (nearly) all tiles are 32-row ones, the last of them (about two
+    // rounds of items) go out one block per item, so that the end of the
+    // queue balances at a fine grain (MI355X: down 0.725 -> 0.705 ms at 401
+    // tokens, -3% at 200 and 1024; with many taller tiles it did not help)
+    const int ntail = (skinny && nbs > 1) ? min(nsmall, (2 * grid + pt1 - 1) / pt1) : 0;
+    nsm = nsmall - ntail;
+    items_big = nbig * ptb;
+    items_mid = items_big + nsm * pts;
+    total = items_mid + ntail * pt1;
+  }
+  // tile index, first output feature and feature blocks of item it
+  __device__ __forceinline__ void decode(int it, int *ti, int *n0, int *nb) const {
+    int nbw;
+    if (it < items_big) {
+      *ti = it / ptb;
+      *n0 = (it - *ti * ptb) * FIB;
+      nbw = nbb;
+    } else if (it < items_mid) {
+      const int is = it - items_big;
+      const int q = is / pts;
+      *ti = nbig + q;
+      *n0 = (is - q * pts) * FIS;
+      nbw = nbs;
+    } else {
+      const int is = it - items_mid;
+      const int q = is / pt1;
+      *ti = nbig + nsm + q;
+      *n0 = (is - q * pt1) * FEAT;
+      nbw = 1;
+    }
+    *nb = min(nbw, (N - *n0 + FEAT - 1) / FEAT);
+  }
+};
+
 template <bool GATEUP>
 __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kGgRing];
-  // the queue head is passed through the idle ring between items
+  // the next item (tile index, first feature, blocks; tile -1 = none left)
+  // is passed from thread 0 through the idle ring between items
   int *next_item = reinterpret_cast<int *>(ring);
   const uint32_t ring_lds = lds_addr(ring);
-  // output features per item: half the weight rows for gate/up (gate and up
-  // rows of the same features), all of them for down
-  const int FEAT = GATEUP ? a.wr / 2 : a.wr;
-  // items of taller tiles first (the list is tallest first), then of the
-  // 32-row tiles; the 32-row tiles take nb_skinny blocks per item when the
-  // taller ones are at most an eighth as many (on MI355X, 4 blocks were
-  // best there and 2 elsewhere, for 200 to 8192 tokens)
-  const int nsmall = *a.n_small;
-  const int nbig = *a.ntiles - nsmall;
-  const bool skinny = nbig * 8 <= nsmall;
-  int nbb = a.nb, nbs = skinny ? a.nb_skinny : a.nb;
-  // with few tiles, halve the blocks per item until at least half the
-  // workgroups have an item: a workgroup of a half-idle chip streams faster
-  // than its even share, so long items on half of them still pay (measured:
-  // 11 experts 0.175 -> 0.123 ms with the halving, 43 experts 4% slower if
-  // every workgroup had to get one).  Block counts above one divide the
-  // feature blocks of a tile.
-  const int pt1 = (a.N + FEAT - 1) / FEAT;
-  while ((nbb > 1 || nbs > 1) &&
-         2 * (nbig * (pt1 / nbb) + nsmall * (pt1 / nbs)) < (int)gridDim.x) {
-    if (nbs >= nbb)
-      nbs >>= 1;
-    else
-      nbb >>= 1;
-  }
-  const int FIB = FEAT * nbb, FIS = FEAT * nbs;  // output features per item
-  const int ptb = (a.N + FIB - 1) / FIB, pts = (a.N + FIS - 1) / FIS;
-  // when (nearly) all tiles are 32-row ones, the last of them (about two
-  // rounds of items) go out one block per item, so that the end of the queue
-  // balances at a fine grain (MI355X: down 0.725 -> 0.705 ms at 401 tokens,
-  // -3% at 200 and 1024; with many taller tiles it did not help)
-  const int ntail =
-      (skinny && nbs > 1) ? min(nsmall, (2 * (int)gridDim.x + pt1 - 1) / pt1) : 0;
-  const int nsm = nsmall - ntail;
-  const int items_big = nbig * ptb;
-  const int items_mid = items_big + nsm * pts;
-  const int total = items_mid + ntail * pt1;
   // two queues (TwoQueue): the items of the first n_multi tiles, whose
   // experts have several tiles, and the rest.  A compute item counts as 1.5
   // stream items for gate/up and 2.25 for down: on MI355X, 8192 Zipf-routed
@@ -445,49 +487,50 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   // (1 to 2.5 all helped, 1.5 best) and down 1.12-1.14 -> 1.05-1.07 ms (1:
   // 1.09, 1.5: 1.08-1.09, 2: 1.12, 2.25: 1.05-1.07, 2.5: 1.09, 3: 1.11 -- not
   // monotonic, so tuned to this workload); 401 and 2048 tokens unchanged.
-  TwoQueue queue(*a.n_multi * ptb, total, GATEUP ? MOE_SSW4_GU : MOE_SSW4_DN);
+  const GgDispatch<GATEUP> D(a);
+  TwoQueue queue(vreg(*a.n_multi) * D.ptb, D.total, GATEUP ? MOE_SSW4_GU : MOE_SSW4_DN, D.grid);
   for (;;) {
-    if (threadIdx.x == 0) *next_item = queue.next(a.counter, a.counter_s);
+    if (threadIdx.x == 0) {
+      const int it = queue.next(a.counter, a.counter_s);
+      int ti = -1, n0 = 0, nb = 0;
+      if (it < D.total) {
+        D.decode(it, &ti, &n0, &nb);
+      } else {
+        queue_release(a.counter, a.counter_s, a.done);
+      }
+      next_item[0] = ti;
+      next_item[1] = n0;
+      next_item[2] = nb;
+      next_item[3] = a.K;
+    }
     __syncthreads();
     // read before gg_item's first barrier (its loads overwrite it); uniform,
-    // so the tile fetch below is a scalar load
-    const int it = __builtin_amdgcn_readfirstlane(*next_item);
-    if (it >= total) break;
-    int ti, n0, nbw;
-    if (it < items_big) {
-      ti = it / ptb;
-      n0 = (it - ti * ptb) * FIB;
-      nbw = nbb;
-    } else if (it < items_mid) {
-      const int is = it - items_big;
-      const int q = is / pts;
-      ti = nbig + q;
-      n0 = (is - q * pts) * FIS;
-      nbw = nbs;
-    } else {
-      const int is = it - items_mid;
-      const int q = is / pt1;
-      ti = nbig + nsm + q;
-      n0 = (is - q * pt1) * FEAT;
-      nbw = 1;
-    }
-    const int nb = min(nbw, (a.N - n0 + FEAT - 1) / FEAT);
+    // so the tile fetch below is a scalar load.  The reduction length also
+    // comes through LDS: read from the kernel arguments, everything derived
+    // from it was hoisted out of the loop and held in scalar registers for
+    // the kernel's lifetime, more than fit.
+    const int ti = __builtin_amdgcn_readfirstlane(next_item[0]);
+    if (ti < 0) break;
+    const int n0 = __builtin_amdgcn_readfirstlane(next_item[1]);
+    const int nb = __builtin_amdgcn_readfirstlane(next_item[2]);
+    GgArgs ai = a;
+    ai.K = __builtin_amdgcn_readfirstlane(next_item[3]);
     const Tile t = a.tiles[ti];
     if (a.wr == 128) {
-      gg_item_any<GATEUP, 1, 128>(a, t, n0, nb, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 128>(ai, t, n0, nb, ring, ring_lds);
     } else if (a.wr == 64) {
-      gg_item_any<GATEUP, 1, 64>(a, t, n0, nb, ring, ring_lds);
+      gg_item_any<GATEUP, 1, 64>(ai, t, n0, nb, ring, ring_lds);
     } else {
       switch (tile_class(t)) {
         case 8:
-        case 6: gg_item_any<GATEUP, 8>(a, t, n0, nb, ring, ring_lds); break;
-        case 4: gg_item_any<GATEUP, 4>(a, t, n0, nb, ring, ring_lds); break;
-        case 2: gg_item_any<GATEUP, 2>(a, t, n0, nb, ring, ring_lds); break;
-        default: gg_item_any<GATEUP, 1>(a, t, n0, nb, ring, ring_lds); break;
+        case 6: gg_item_any<GATEUP, 8>(ai, t, n0, nb, ring, ring_lds); break;
+        case 4: gg_item_any<GATEUP, 4>(ai, t, n0, nb, ring, ring_lds); break;
+        case 2: gg_item_any<GATEUP, 2>(ai, t, n0, nb, ring, ring_lds); break;
+        default: gg_item_any<GATEUP, 1>(ai, t, n0, nb, ring, ring_lds); break;
       }
     }
-    // the ring (and the queue head in it) is rewritten only after every wave
-    // has passed this barrier
+    // the ring (and the item in it) is rewritten only after every wave has
+    // passed this barrier
     __syncthreads();
   }
 }
@@ -556,6 +599,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.d;
     g.counter = &L.sch->counter[0];
     g.counter_s = &L.sch->counter_s[0];
+    g.done = &L.sch->done[0];
     g.wr = item_weight_rows(L, L.f, 2);
     g.nb = 1;
     g.nb_skinny = 1;
@@ -571,6 +615,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.f;
     g.counter = &L.sch->counter[1];
     g.counter_s = &L.sch->counter_s[1];
+    g.done = &L.sch->done[1];
     g.wr = item_weight_rows(L, L.d, 1);
     g.nb = item_blocks(g.wr, L.d, 1, 2);
     g.nb_skinny = item_blocks(g.wr, L.d, 1, 4);

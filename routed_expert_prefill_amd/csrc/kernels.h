@@ -14,10 +14,12 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
                               int32_t *route_rows, int32_t *ws, hipStream_t stream);
 size_t route_build_ws_bytes(int R, int E);
 
-// shared (fp32 [T,d]) and out_bf16 may be null; out may be null if out_bf16 is not.
+// row_limit (one int32: rows of y at or past it are never read), shared
+// (fp32 [T,d]) and out_bf16 may be null; out may be null if out_bf16 is not.
 hipError_t launch_combine(const float *y, const int32_t *route_rows, const float *topk_w,
-                          const uint8_t *mask, const float *shared, int T, int k, int d,
-                          float *out, uint16_t *out_bf16, hipStream_t stream);
+                          const uint8_t *mask, const int32_t *row_limit, const float *shared,
+                          int T, int k, int d, float *out, uint16_t *out_bf16,
+                          hipStream_t stream);
 
 hipError_t launch_route_topk(const float *logits, const float *bias, int T, int E, int k,
                              int32_t *ids, float *gates, int grid_cap, hipStream_t stream);

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -68,6 +68,8 @@ def test_route_build_errors(lib):
     assert _rb(lib, E=0) == _lib.MOE_EUNSUPPORTED
     assert _rb(lib, E=257) == _lib.MOE_EUNSUPPORTED
     assert _rb(lib, k=17, E=64) == _lib.MOE_EUNSUPPORTED
+    assert _rb(lib, k=5, E=4) == _lib.MOE_EUNSUPPORTED  # k > E, as moe_grouped_ffn and moe_route_topk
+    assert _rb(lib, k=4, E=4, ids=0) == _lib.MOE_EINVAL  # k == E passes the shape check
     assert _rb(lib, ids=A + 4) == _lib.MOE_EALIGN
     assert _rb(lib, mask=A + 1) == _lib.MOE_EALIGN
     assert _rb(lib, ws=0) == _lib.MOE_EWORKSPACE
@@ -126,8 +128,8 @@ def test_ffn_stage_errors(lib):
 
 
 def test_combine_errors(lib):
-    c = lambda y=A, rr=A, w=A, m=0, T=4, k=2, d=64, out=A: lib.moe_combine(  # noqa: E731
-        y, rr, w, m or None, T, k, d, out, None)
+    c = lambda y=A, rr=A, w=A, m=0, lim=0, T=4, k=2, d=64, out=A: lib.moe_combine(  # noqa: E731
+        y, rr, w, m or None, lim or None, T, k, d, out, None)
     assert c(y=0) == _lib.MOE_EINVAL
     assert c(out=0) == _lib.MOE_EINVAL
     assert c(T=0) == _lib.MOE_EINVAL
@@ -135,11 +137,13 @@ def test_combine_errors(lib):
     assert c(k=17) == _lib.MOE_EUNSUPPORTED
     assert c(w=A + 4) == _lib.MOE_EALIGN
     assert c(m=A + 3) == _lib.MOE_EALIGN
+    assert c(lim=A + 2) == _lib.MOE_EALIGN  # the row limit is one int32: 4-byte aligned
+    assert c(lim=A + 4, y=0) == _lib.MOE_EINVAL  # 4-byte aligned passes the alignment check
 
 
 def test_combine_shared_errors(lib):
-    c = lambda y=A, rr=A, w=A, m=0, sh=0, T=4, k=2, d=64, out=A, ob=0: lib.moe_combine_shared(  # noqa: E731
-        y, rr, w, m or None, sh or None, T, k, d, out or None, ob or None, None)
+    c = lambda y=A, rr=A, w=A, m=0, lim=0, sh=0, T=4, k=2, d=64, out=A, ob=0: lib.moe_combine_shared(  # noqa: E731
+        y, rr, w, m or None, lim or None, sh or None, T, k, d, out or None, ob or None, None)
     assert c(y=0) == _lib.MOE_EINVAL
     assert c(out=0, ob=0) == _lib.MOE_EINVAL  # no output at all
     assert c(T=0) == _lib.MOE_EINVAL
@@ -147,6 +151,7 @@ def test_combine_shared_errors(lib):
     assert c(k=17) == _lib.MOE_EUNSUPPORTED
     assert c(sh=A + 4) == _lib.MOE_EALIGN
     assert c(out=0, ob=A + 2) == _lib.MOE_EALIGN
+    assert c(lim=A + 1) == _lib.MOE_EALIGN
 
 
 def test_quant_errors(lib):

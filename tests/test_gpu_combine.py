@@ -112,3 +112,39 @@ def test_shared_output_form(seed, T, k, d, p):
     # bf16 only
     none2, ob2 = _run_shared(y, rr, w, mask, shared, want_fp32=False)
     assert none2 is None and np.array_equal(ob2, ob)
+
+
+def test_row_limit_skips_trailing_rows():
+    """With a row limit n, a route whose row is n or more is never read, like
+    a masked one: the output equals the combine with those routes masked,
+    bit for bit, even with NaN in the skipped rows and gates."""
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    T, k, d = 97, 6, 512
+    y, rr, w, mask = _case(20, T, k, d, 0.1)
+    n = (T * k * 3) // 4
+    yp, wp = y.copy(), w.copy().reshape(-1)
+    beyond = rr >= n
+    yp[n:] = np.nan
+    wp[beyond] = np.nan
+    lim = torch.tensor([n], dtype=torch.int32, device="cuda:0")
+    for m in (mask, None):
+        got = rep.combine(np_dev(yp), np_dev(rr), np_dev(wp.reshape(T, k)),
+                          None if m is None else np_dev(m), row_limit=lim)
+        eff = (np.ones((T, k), np.uint8) if m is None else m).copy().reshape(-1)
+        eff[beyond] = 0
+        want = _run(y, rr, w, eff.reshape(T, k))
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    # the shared-output form honours the same bound
+    sh = np.random.default_rng(21).standard_normal((T, d)).astype(np.float32)
+    o1, _ = rep.combine_shared(np_dev(yp), np_dev(rr), np_dev(wp.reshape(T, k)), np_dev(mask),
+                               np_dev(sh), row_limit=lim)
+    eff = mask.copy().reshape(-1)
+    eff[beyond] = 0
+    o2, _ = rep.combine_shared(np_dev(y), np_dev(rr), np_dev(w), np_dev(eff.reshape(T, k)),
+                               np_dev(sh))
+    torch.cuda.synchronize()
+    assert np.array_equal(o1.cpu().numpy().view(np.uint32), o2.cpu().numpy().view(np.uint32))

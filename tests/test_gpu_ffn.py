@@ -292,3 +292,79 @@ def test_deterministic_and_zero_input():
     zero = run(bf16_dev(np.zeros_like(x)), *args)
     torch.cuda.synchronize()
     assert torch.all(zero.view(torch.int32) == 0)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_active_routes_with_out_of_range_ids_add_exact_zeros(fp8):
+    """An active route whose id lies outside [0, E) counts as masked on both
+    sides: the route build sends it to the trailing bin, the FFN never writes
+    its row of y (NaN-filled here), the combine reads no row at or past
+    offsets[E], and the oracle skips it.  Tokens whose only active routes are
+    such ids get exactly +0.0."""
+    E, d, f = 12, 256, 256
+    counts = [30, 0, 7, 64, 1, 0, 40, 3, 12, 0, 33, 5]
+    ids, mask = routing_with_counts(counts, 6, seed=60, masked_extra=11, invalid_extra=17)
+    T, k = ids.shape
+    ids = ids.copy()
+    bad = np.flatnonzero(ids.reshape(-1) >= E)
+    ids.reshape(-1)[bad[::2]] = -7  # negative ids too
+    # a token whose routes are all active and all out of range
+    ids = np.concatenate([ids, np.array([[E + 1, -1, 2 ** 20, -(2 ** 30), E, E + 5]], np.int32)])
+    mask = np.concatenate([mask, np.ones((1, 6), np.uint8)])
+    T += 1
+    w = np.random.default_rng(61).random((T, k)).astype(np.float32)
+    x = _x(T, d, 62)
+    W = _weights(E, d, f, fp8, 63)
+    run, out = _run(ids, w, mask, x, W, E, fp8, y_fill=float("nan"))
+    assert np.all(np.isfinite(out))
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+    valid = (mask != 0) & (ids >= 0) & (ids < E)
+    none = np.flatnonzero(valid.sum(axis=1) == 0)
+    assert T - 1 in none
+    for t in none:
+        assert np.all(out[t] == 0) and not np.any(np.signbit(out[t])), t
+    n_act = int(run.rt.offsets[E].item())
+    assert n_act == int(valid.sum())
+    y = run.y.cpu().numpy()
+    assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_stage_calls_run_again_on_one_plan(fp8):
+    """moe_ffn_gate_up and moe_ffn_down may run again without a new
+    moe_ffn_plan (each persistent GEMM resets its queue heads when its last
+    workgroup leaves); the second pass writes the same bits."""
+    import torch
+
+    import routed_expert_prefill_amd as rep
+
+    E, d, f = len(QUEUE_COUNTS), 256, 256
+    ids, mask = routing_with_counts(QUEUE_COUNTS, 6, seed=70, masked_extra=7)
+    T, k = ids.shape
+    x = _x(T, d, 71)
+    Wn = _weights(E, d, f, fp8, 72)
+    Wd = _dev_weights(Wn, fp8)
+    rt = rep.route_build(np_dev(ids), np_dev(mask), E)
+    desc = rep.ffn_desc(T, k, E, d, f, fp8)
+    ws = rep._ffn_ws(desc, torch.device("cuda:0"), None)
+    y = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda:0")
+    xd = bf16_dev(x)
+    rep.ffn_plan(desc, xd, rt.offsets, ws)
+    rep.ffn_gate_up(desc, xd, rt.sorted_routes, Wd["wg"], Wd["wu"], Wd.get("sg"), Wd.get("su"), ws)
+    rep.ffn_down(desc, rt.offsets, Wd["wd"], Wd.get("sd"), y, ws)
+    torch.cuda.synchronize()
+    first = y.clone()
+    n_act = int(rt.offsets[E].item())
+    for _ in range(2):
+        y.fill_(float("nan"))
+        rep.ffn_gate_up(desc, xd, rt.sorted_routes, Wd["wg"], Wd["wu"], Wd.get("sg"), Wd.get("su"),
+                        ws)
+        rep.ffn_down(desc, rt.offsets, Wd["wd"], Wd.get("sd"), y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(first[:n_act].view(torch.int32), y[:n_act].view(torch.int32))
+        assert torch.all(torch.isnan(y[n_act:]))
+    w = np.random.default_rng(73).random((T, k)).astype(np.float32)
+    out = rep.combine(y, rt.route_rows, np_dev(w), np_dev(mask)).cpu().numpy().astype(np.float64)
+    ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(Wn), E, fp8=fp8)
+    _check(out, ref, FP8_TOL if fp8 else BF16_TOL)

@@ -47,9 +47,11 @@ def test_owner_partials_sum_to_full_output():
         none = m.sum(axis=1) == 0
         assert np.all(out_g[none].view(np.uint32) == 0)  # exact +0.0
         ref_g = omoe.moe_ref_per_token(r.x, r.topk_ids, r.topk_w, m, omoe.dict_source(W), wl.E)
+        assert np.abs(out_g - ref_g).max() <= 2e-2
         assert rel_frob(out_g, ref_g) <= 1e-3
         parts.append(out_g.astype(np.float32))
     total = np.zeros_like(parts[0])
     for p_ in parts:
         total += p_
     assert rel_frob(total, full) <= 1e-6
+    assert np.abs(total - full).max() <= 1e-6 * np.abs(full).max()

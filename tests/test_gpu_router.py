@@ -64,5 +64,4 @@ def test_workload_logits_match_generator(name):
     gi, gw = _gpu(z, wl.k)
     assert np.array_equal(gi, r.topk_ids)
     assert np.all(np.abs(gw - r.topk_w) <= np.spacing(r.topk_w))
-    if wl.T <= 2048:
-        _check(z, wl.k)
+    _check(z, wl.k)  # and against the fp64 router oracle, at every size
