@@ -368,3 +368,33 @@ def test_stage_calls_run_again_on_one_plan(fp8):
     out = rep.combine(y, rt.route_rows, np_dev(w), np_dev(mask)).cpu().numpy().astype(np.float64)
     ref = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(Wn), E, fp8=fp8)
     _check(out, ref, FP8_TOL if fp8 else BF16_TOL)
+
+
+# Experts of 257 to 2000 rows at the workloads' width (d = 4096, f = 2048):
+# 35 256-row tiles of multi-tile experts (560 compute-queue items per
+# projection), including the 208- and 220-row last tiles of the 2000- and
+# 1500-row experts, beside remainder tiles of 13 to 188 rows on the stream
+# queue; compared in full with the expert-major oracle.
+TALL_COUNTS = [1100, 1037, 900, 0, 1300, 257, 2000, 700, 1500, 600]
+
+
+def test_compute_bound_tiles():
+    from threadpoolctl import threadpool_limits
+
+    E, d, f = len(TALL_COUNTS), 4096, 2048
+    ids, mask = routing_with_counts(TALL_COUNTS, 6, seed=80, masked_extra=40)
+    T, k = ids.shape
+    w = np.random.default_rng(81).random((T, k)).astype(np.float32)
+    x = _x(T, d, 82)
+    W = _weights(E, d, f, False, 83)
+    run, out = _run(ids, w, mask, x, W, E, False, y_fill=float("nan"))
+    n_act = int(run.rt.offsets[E].item())
+    y = run.y.cpu().numpy()
+    assert np.all(np.isnan(y[n_act:])) and not np.any(np.isnan(y[:n_act]))
+    with threadpool_limits(limits=16):
+        ref_out, ref_y, _ = omoe.moe_ref_blocked(x, ids, w, mask, omoe.dict_source(W), E)
+    _check(y[:n_act].astype(np.float64), ref_y[:n_act], BF16_TOL)
+    _check(out, ref_out, BF16_TOL)
+    toks = [0, T // 2, T - 1]
+    ref_tok = omoe.moe_ref_per_token(x, ids, w, mask, omoe.dict_source(W), E, tokens=toks)
+    _check(out[toks], ref_tok, BF16_TOL)

@@ -27,7 +27,7 @@ def test_kernels_use_no_scratch_and_do_not_spill(src):
         assert r["SGPRs Spill"] == 0, (kern, r)
         assert r["VGPRs Spill"] == 0, (kern, r)
         if "grouped_gemm" in kern:
-            assert r["Occupancy"] >= 2, (kern, r)
+            assert r["Occupancy"] >= 2, (kern, r)  # two waves per SIMD cover each other
 
 
 def test_abi_under_host_sanitizers():
