@@ -52,7 +52,8 @@ typedef enum moe_status {
   MOE_EUNSUPPORTED = -2, /* E > 256, k > 16 or k > E, d or f not a multiple of 128, dtype mix */
   MOE_EALIGN = -3,       /* a device base pointer is not 16-byte aligned */
   MOE_EWORKSPACE = -4,   /* workspace pointer null or smaller than the size query */
-  MOE_EHIP = -5          /* the HIP runtime reported an error */
+  MOE_EHIP = -5,         /* the HIP runtime reported an error */
+  MOE_ETOOLARGE = -6     /* larger than the fixed device scratch of a no-allocation call */
 } moe_status;
 
 /* Weight storage formats. */
@@ -119,6 +120,27 @@ int moe_route_build(const int32_t *topk_ids, const uint8_t *route_mask, int T, i
                     int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
                     int32_t *route_rows, void *workspace, size_t workspace_bytes,
                     moe_stream_t stream);
+
+/* ------------------------------------------------------------ route build, no allocation
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * route build as moe_route_build, with the same outputs bit for bit, but
+ * without a workspace.  Its kernels use a fixed device array of the library
+ * (MOE_ROUTE_NOALLOC_MAX_ROUTES routes' worth of chunk histograms, about
+ * 1 MiB per GPU, held until the process ends); the call allocates and frees
+ * nothing.  The caller still owns topk_ids, route_mask and the four outputs.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams) race and must not be issued.  Nothing in the
+ * array has to be cleared between calls (each call writes what it reads).
+ * Arguments as for moe_route_build.
+ * Errors: as moe_route_build, and MOE_ETOOLARGE if T*k exceeds
+ *         MOE_ROUTE_NOALLOC_MAX_ROUTES.
+ */
+#define MOE_ROUTE_NOALLOC_MAX_ROUTES (1 << 20)
+int moe_route_build_noalloc(const int32_t *topk_ids, const uint8_t *route_mask, int T, int k,
+                            int E, int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                            int32_t *route_rows, moe_stream_t stream);
 
 /* ------------------------------------------------------------ grouped FFN
  * Grouped gate/up GEMM + SwiGLU + grouped down GEMM over expert-contiguous

@@ -16,7 +16,7 @@ from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_E4M3_ROW, MOE_W_BF16, MOE_W_FP8_E4M
                    LibraryNotBuilt, MoeFfnDesc)
 
 __all__ = [
-    "route_topk", "route_build", "grouped_ffn", "combine", "combine_shared", "quant_rows_fp8", "MoEPrefill", "RouteTable",
+    "route_topk", "route_build", "route_build_noalloc", "grouped_ffn", "combine", "combine_shared", "quant_rows_fp8", "MoEPrefill", "RouteTable",
     "ffn_desc", "ffn_plan", "ffn_gate_up", "ffn_down", "LibraryNotBuilt", "load_library",
 ]
 
@@ -108,6 +108,31 @@ def route_build(topk_ids, route_mask, E: int, out: Optional[RouteTable] = None,
                              _ptr(out.offsets), _ptr(out.sorted_routes), _ptr(out.route_rows),
                              _ptr(workspace), workspace.numel(), _stream())
     _lib.check(rc, "moe_route_build")
+    return out
+
+
+def route_build_noalloc(topk_ids, route_mask, E: int, out: Optional[RouteTable] = None) -> RouteTable:
+    """moe_route_build_noalloc: the route build on the library's own device
+    scratch (no workspace); at most MOE_ROUTE_NOALLOC_MAX_ROUTES routes.  The
+    outputs are allocated here unless given; the C call allocates nothing."""
+    torch = _torch()
+    lib = _lib.load()
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    if route_mask is not None:
+        _need(route_mask, "route_mask", torch.uint8, 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if out is None:
+        out = RouteTable(
+            counts=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            offsets=torch.empty(E + 2, dtype=torch.int32, device=dev),
+            sorted_routes=torch.empty(T * k, dtype=torch.int32, device=dev),
+            route_rows=torch.empty(T * k, dtype=torch.int32, device=dev),
+        )
+    rc = lib.moe_route_build_noalloc(_ptr(topk_ids), _ptr(route_mask), T, k, E, _ptr(out.counts),
+                                     _ptr(out.offsets), _ptr(out.sorted_routes),
+                                     _ptr(out.route_rows), _stream())
+    _lib.check(rc, "moe_route_build_noalloc")
     return out
 
 

@@ -15,6 +15,8 @@ MOE_EUNSUPPORTED = -2
 MOE_EALIGN = -3
 MOE_EWORKSPACE = -4
 MOE_EHIP = -5
+MOE_ETOOLARGE = -6
+MOE_ROUTE_NOALLOC_MAX_ROUTES = 1 << 20
 
 MOE_W_BF16 = 0
 MOE_W_FP8_E4M3_B128 = 1
@@ -27,6 +29,7 @@ EXPORTED = [
     "moe_grouped_ffn_workspace", "moe_grouped_ffn",
     "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
     "moe_combine", "moe_quant_rows_fp8", "moe_route_topk", "moe_combine_shared",
+    "moe_route_build_noalloc",
 ]
 
 
@@ -62,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.moe_route_build_workspace.argtypes = [i32, i32, i32]
     lib.moe_route_build.restype = i32
     lib.moe_route_build.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_build_noalloc.restype = i32
+    lib.moe_route_build_noalloc.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_grouped_ffn_workspace.restype = sz
     lib.moe_grouped_ffn_workspace.argtypes = [ctypes.POINTER(MoeFfnDesc)]
     lib.moe_grouped_ffn.restype = i32

@@ -112,6 +112,8 @@ const char *moe_status_string(int status) {
     case MOE_EALIGN: return "MOE_EALIGN: device pointer not 16-byte aligned";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
     case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    case MOE_ETOOLARGE:
+      return "MOE_ETOOLARGE: larger than the fixed device scratch of a no-allocation call";
     default: return "unknown moe_status";
   }
 }
@@ -140,6 +142,22 @@ int moe_route_build(const int32_t *topk_ids, const uint8_t *route_mask, int T, i
                                              sorted_routes, route_rows,
                                              static_cast<int32_t *>(workspace),
                                              static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_build_noalloc(const int32_t *topk_ids, const uint8_t *route_mask, int T, int k,
+                            int E, int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                            int32_t *route_rows, moe_stream_t stream) {
+  static_assert(MOE_ROUTE_NOALLOC_MAX_ROUTES == moe::kRouteNoAllocMaxR, "one limit");
+  if (!topk_ids || !counts || !offsets || !sorted_routes || !route_rows) return MOE_EINVAL;
+  if (T < 1 || k < 1 || (long long)T * k >= (1LL << 31)) return MOE_EINVAL;
+  if (E < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_EUNSUPPORTED;
+  if ((long long)T * k > MOE_ROUTE_NOALLOC_MAX_ROUTES) return MOE_ETOOLARGE;
+  if (misaligned(topk_ids) || misaligned(counts) || misaligned(offsets) ||
+      misaligned(sorted_routes) || misaligned(route_rows) || (route_mask && misaligned(route_mask)))
+    return MOE_EALIGN;
+  return status_from(moe::launch_route_build_noalloc(topk_ids, route_mask, T * k, E, counts,
+                                                     offsets, sorted_routes, route_rows,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_grouped_ffn_workspace(const moe_ffn_desc *desc) {

@@ -14,6 +14,13 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
                               int32_t *route_rows, int32_t *ws, hipStream_t stream);
 size_t route_build_ws_bytes(int R, int E);
 
+// The route build on the library's own device scratch (no workspace, no
+// allocation), for up to kRouteNoAllocMaxR routes.
+constexpr int kRouteNoAllocMaxR = 1 << 20;
+hipError_t launch_route_build_noalloc(const int32_t *ids, const uint8_t *mask, int R, int E,
+                                      int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                                      int32_t *route_rows, hipStream_t stream);
+
 // row_limit (one int32: rows of y at or past it are never read), shared
 // (fp32 [T,d]) and out_bf16 may be null; out may be null if out_bf16 is not.
 hipError_t launch_combine(const float *y, const int32_t *route_rows, const float *topk_w,

@@ -9,6 +9,8 @@
 //      route order, finds equal keys among the 64 lanes with one ballot per
 //      key bit, and ranks each lane among its earlier peers.
 // Results are integers and do not depend on scheduling.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace moe {
@@ -265,6 +267,54 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
 
 size_t route_build_ws_bytes(int R, int E) {
   return (size_t)2 * route_chunks(R) * (E + 1) * sizeof(int32_t);
+}
+
+// ------------------------------------------------------------------ no allocation
+
+// The route build for callers that cannot allocate: the chunk histograms and
+// chunk bases live in this file-scope device array instead of a caller's
+// workspace.  Each GPU holds its own copy until the process ends; every call
+// on a GPU uses that GPU's copy.  Every word the kernels read there is
+// written earlier in the same call (histograms, then bases), so nothing has
+// to be cleared between calls; calls that overlap on one GPU race.
+static __device__ __align__(256) int32_t scratch[2 * (kRouteNoAllocMaxR / kChunk) * kMaxBins];
+static_assert(kRouteNoAllocMaxR % kChunk == 0, "whole chunks");
+static_assert(sizeof(scratch) >= 2 * (kRouteNoAllocMaxR / kChunk) * (size_t)kMaxBins * 4,
+              "room for the chunk histograms and bases of the largest call");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+int32_t *scratch_dev[kMaxDevices];  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+hipError_t route_build_scratch(int32_t **ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    // the host-side name `scratch` is not a device address: look the
+    // device's copy up once, with that device current
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    scratch_dev[dev] = static_cast<int32_t *>(p);
+  }
+  *ptr = scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_route_build_noalloc(const int32_t *ids, const uint8_t *mask, int R, int E,
+                                      int32_t *counts, int32_t *offsets, int32_t *sorted_routes,
+                                      int32_t *route_rows, hipStream_t stream) {
+  if (R > kRouteNoAllocMaxR) return hipErrorInvalidValue;  // the caller checks first
+  int32_t *ws = nullptr;
+  const hipError_t err = route_build_scratch(&ws);
+  if (err != hipSuccess) return err;
+  return launch_route_build(ids, mask, R, E, counts, offsets, sorted_routes, route_rows, ws,
+                            stream);
 }
 
 }  // namespace moe

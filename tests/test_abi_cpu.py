@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.moe_status_string(code).decode().startswith("MOE_")
     assert b"unknown" in lib.moe_status_string(7)
 
@@ -74,6 +74,24 @@ def test_route_build_errors(lib):
     assert _rb(lib, mask=A + 1) == _lib.MOE_EALIGN
     assert _rb(lib, ws=0) == _lib.MOE_EWORKSPACE
     assert _rb(lib, wsb=16) == _lib.MOE_EWORKSPACE
+
+
+def _rbn(lib, ids=A, mask=0, T=8, k=2, E=4, c=A, o=A, s=A, r=A):
+    return lib.moe_route_build_noalloc(ids, mask or None, T, k, E, c, o, s, r, None)
+
+
+def test_route_build_noalloc_errors(lib):
+    assert _rbn(lib, ids=0) == _lib.MOE_EINVAL
+    assert _rbn(lib, c=0) == _lib.MOE_EINVAL
+    assert _rbn(lib, T=0) == _lib.MOE_EINVAL
+    assert _rbn(lib, E=257) == _lib.MOE_EUNSUPPORTED
+    assert _rbn(lib, k=5, E=4) == _lib.MOE_EUNSUPPORTED
+    assert _rbn(lib, T=1 << 28, k=16, E=256) == _lib.MOE_EINVAL  # T*k >= 2^31
+    # beyond the fixed scratch: rejected before any HIP call
+    big = _lib.MOE_ROUTE_NOALLOC_MAX_ROUTES
+    assert _rbn(lib, T=big // 4 + 1, k=4, E=256) == _lib.MOE_ETOOLARGE
+    assert _rbn(lib, T=big // 4, k=4, E=256, ids=A + 4) == _lib.MOE_EALIGN  # the largest size passes
+    assert _rbn(lib, mask=A + 2) == _lib.MOE_EALIGN
 
 
 def _desc(T=32, k=6, E=16, d=512, f=256, w=0, a=0):
