@@ -9,9 +9,7 @@
 //
 // Rows of up to 4096 elements: one wave per row; longer rows (up to
 // kQMaxCols): one workgroup per row.  Either way a row is read once into
-// registers, reduced, then encoded and written; the quotients are formed by
-// a reciprocal multiply where that provably gives the same code
-// (quant_e4m3), by IEEE division elsewhere.
+// registers, reduced, then encoded and written.
 #include "kernels.h"
 
 namespace moe {
@@ -32,43 +30,6 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   // subnormal range: multiples of 2^-9 (8 * 2^-9 = 2^-6 encodes as 0x08)
   const float s = __uint_as_float(a) * 512.0f;
   return sign | (uint32_t)__builtin_rintf(s);
-}
-
-// q = e4m3_rne_saturate(fl32(v / sc)) without a division for nearly every
-// element.  rcp = fl32(1 / sc); exact: the row needs the division throughout
-// (sc not a normal float, or rcp not finite).
-//
-// y = v * rcp differs from fl32(v / sc) by a few units in the last place
-// (two roundings of relative size 2^-24 each against one), i.e. by at most a
-// handful of consecutive fp32 bit patterns.  E4M3 rounding is monotone and
-// changes only at the midpoints between neighbouring codes, which in the
-// normal range are the patterns whose low 20 bits are 0x80000.  So where y
-// lies in the normal range and more than 16 patterns from a midpoint, the
-// quotient rounds to y's code; within the window (ties included), in the
-// subnormal-code range and for rows flagged exact, the quotient is formed by
-// IEEE division.  Values at or beyond 448 saturate either way.
-__device__ __forceinline__ uint32_t quant_e4m3(float v, float sc, float rcp, bool exact) {
-  const uint32_t b = __float_as_uint(v * rcp);
-  const uint32_t a = b & 0x7fffffffu;
-  const bool sat = a >= 0x43e00000u;   // 448 and beyond: saturated either way
-  const bool norm = a >= 0x3c800000u;  // 2^-6: normal codes
-  const uint32_t enc = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  // key < 32 <=> the slow path: within 16 patterns of a midpoint (normal
-  // codes), any nonzero subnormal code, or an exact row; selects, not
-  // branches, so that the only branch left is the rare slow path
-  uint32_t key = norm ? (a & 0xfffffu) - 0x7fff0u : (a != 0u ? 0u : 0xffffffffu);
-  key = sat ? 0xffffffffu : key;
-  key = exact ? 0u : key;
-  uint32_t code = (sat ? 0x7eu : (norm ? enc : 0u)) | ((b >> 24) & 0x80u);
-  if (key < 32u) code = f32_to_e4m3(v / sc);
-  return code;
-}
-
-// The reciprocal of a row scale, and whether the row must divide throughout.
-__device__ __forceinline__ float quant_rcp(float sc, bool *exact) {
-  const float r = 1.0f / sc;
-  *exact = !(sc >= 1.17549435e-38f) || !(r < 3.40282347e38f);  // sc subnormal, r overflowed
-  return r;
 }
 
 constexpr int kQThreads = 256;
@@ -115,8 +76,6 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
     __syncthreads();
     const bool zero = amax == 0.0f;
     const float sc = zero ? 1.0f : amax / 448.0f;
-    bool exact;
-    const float rcp = quant_rcp(sc, &exact);
     if (tid == 0) s[row] = sc;
     uint8_t *dst = q + (size_t)row * cols;
 #pragma unroll
@@ -133,7 +92,7 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
             for (int e = 0; e < 4; ++e) {
               const uint32_t two = (uint32_t)raw[p][h][w + (e >> 1)];
               const uint16_t bits = (e & 1) ? (uint16_t)(two >> 16) : (uint16_t)(two & 0xffffu);
-              const uint32_t code = zero ? 0u : quant_e4m3(bf16_bits_to_f32(bits), sc, rcp, exact);
+              const uint32_t code = zero ? 0u : f32_to_e4m3(bf16_bits_to_f32(bits) / sc);
               packed |= code << (8 * e);
             }
             out[h * 2 + (w >> 1)] = (int)packed;
@@ -176,8 +135,6 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
     for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const bool zero = amax == 0.0f;
     const float sc = zero ? 1.0f : amax / 448.0f;
-    bool exact;
-    const float rcp = quant_rcp(sc, &exact);
     if (lane == 0) s[row] = sc;
     uint8_t *dst = q + (size_t)row * cols;
 #pragma unroll
@@ -192,7 +149,7 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
           for (int e = 0; e < 4; ++e) {
             const uint32_t two = (uint32_t)raw[i][h * 2 + (e >> 1)];
             const uint16_t bits = (e & 1) ? (uint16_t)(two >> 16) : (uint16_t)(two & 0xffffu);
-            const uint32_t code = zero ? 0u : quant_e4m3(bf16_bits_to_f32(bits), sc, rcp, exact);
+            const uint32_t code = zero ? 0u : f32_to_e4m3(bf16_bits_to_f32(bits) / sc);
             packed |= code << (8 * e);
           }
           (h ? out.y : out.x) = packed;
