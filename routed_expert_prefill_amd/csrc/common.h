@@ -53,8 +53,7 @@ struct Schedule {
   int n_small;     // 32-row tiles, the last n_small entries of the list
   int n_multi;     // tiles of experts with more than kTileRows rows, the first n_multi entries
   int counter_s[2];  // second queue heads (items of the other tiles) of the two kernels
-  int done[2];     // workgroups of the gate/up and down kernels that have left their queues
-  int pad[55];     // keeps the tile list 256-byte aligned
+  int pad[57];     // keeps the tile list 256-byte aligned
 };
 static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 256 bytes");
 
@@ -69,10 +68,21 @@ static_assert(sizeof(Schedule) == 256, "the tile list follows the schedule at 25
 // items, between 1/16 and 1/2 of the grid.  Used by thread 0 of a workgroup
 // only.  Both members are forced inline: as calls they kept the object in
 // the private segment (scratch memory) and made the caller save registers.
+//
+// A workgroup never draws again from a queue that has once come back empty
+// (its head only grows), and it stops when both have.  Every workgroup of
+// the grid therefore draws exactly once past the end of each queue, each
+// head ends at its item count + G, and the workgroup whose draw returns that
+// value - 1 made the head's last access of the launch: it sets the head back
+// to 0, so the same stage can run again on the same schedule with no
+// arrival count or fence at the end of the kernel.  All G workgroups must
+// draw until next() returns the end.
 struct TwoQueue {
-  int nc, ns, src;  // src: 0 = compute queue, 1 = stream queue
-  __device__ __forceinline__ TwoQueue(int nc_, int total, int weight4, int G)
-      : nc(nc_), ns(total - nc_) {
+  int nc, ns, G;
+  int src;  // 0 = compute queue, 1 = stream queue
+  int dry;  // bit q set: queue q came back empty
+  __device__ __forceinline__ TwoQueue(int nc_, int total, int weight4, int G_)
+      : nc(nc_), ns(total - nc_), G(G_), dry(0) {
     const int ps =
         nc == 0 ? G
                 : max(G / 16, min(G / 2, (int)((long long)G * 4 * ns /
@@ -82,34 +92,19 @@ struct TwoQueue {
   // the next item, or nc + ns when both queues are empty
   __device__ __forceinline__ int next(int *compute_head, int *stream_head) {
     for (int tries = 0; tries < 2; ++tries) {
-      if (src == 0) {
-        const int q = atomicAdd(compute_head, 1);
-        if (q < nc) return q;
-        src = 1;
-      } else {
-        const int q = atomicAdd(stream_head, 1);
-        if (q < ns) return nc + q;
-        src = 0;
+      if (!((dry >> src) & 1)) {
+        int *head = src ? stream_head : compute_head;
+        const int n = src ? ns : nc;
+        const int q = atomicAdd(head, 1);
+        if (q < n) return src ? nc + q : q;
+        if (q == n + G - 1) __hip_atomic_store(head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dry |= 1 << src;
       }
+      src ^= 1;
     }
     return nc + ns;
   }
 };
-
-// Called by thread 0 of each workgroup of a persistent GEMM after its last
-// queue access.  The last workgroup of the grid to arrive resets the
-// kernel's two queue heads and the arrival count, so the same stage can run
-// again on the same schedule.  The fence orders this workgroup's queue
-// atomics before its arrival; the last arrival therefore follows every
-// queue access of the grid.
-__device__ __forceinline__ void queue_release(int *compute_head, int *stream_head, int *done) {
-  __threadfence();
-  if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
-    atomicExch(compute_head, 0);
-    atomicExch(stream_head, 0);
-    atomicExch(done, 0);
-  }
-}
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (gfx950): lane l
 // supplies row (l % 16) of its operand and the 8 consecutive reduction

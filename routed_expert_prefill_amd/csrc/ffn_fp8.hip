@@ -32,7 +32,6 @@ struct Gg8Args {
   const int *n_multi;  // tiles of experts with several tiles, at the start of the list
   int *counter;        // compute-queue head (TwoQueue)
   int *counter_s;      // stream-queue head
-  int *done;           // workgroups that have left the queues (queue_release)
   int nb;  // feature blocks per item (streamed through one ring fill)
 };
 
@@ -393,8 +392,6 @@ __global__ __launch_bounds__(kG8Threads, 1) void grouped_gemm8_kernel(Gg8Args a)
         ti = it / per_tile;
         n0 = (it - ti * per_tile) * FI;
         nb = min(nbi, (N - n0 + FEAT - 1) / FEAT);
-      } else {
-        queue_release(a.counter, a.counter_s, a.done);
       }
       next_item[0] = ti;
       next_item[1] = n0;
@@ -451,7 +448,6 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.K = L.d;
     g.counter = &L.sch->counter[0];
     g.counter_s = &L.sch->counter_s[0];
-    g.done = &L.sch->done[0];
     g.nb = 1;
     hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
@@ -474,7 +470,6 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.K = L.f;
     g.counter = &L.sch->counter[1];
     g.counter_s = &L.sch->counter_s[1];
-    g.done = &L.sch->done[1];
     // the most blocks of 128 outputs, up to kG8MaxBlocks, that tile d
     // (MI355X, 8192 tokens: down 0.946 -> 0.877 ms with four, 0.884 with two)
     g.nb = kG8MaxBlocks;

@@ -62,7 +62,6 @@ struct GgArgs {
   const int *n_small;  // 32-row tiles at the end of the tile list
   const int *n_multi;  // tiles of experts with several tiles, at the start of the list
   int *counter_s;      // head of the second queue (items of the other tiles)
-  int *done;           // workgroups that have left the queues (queue_release)
 };
 
 constexpr int kGgThreads = 512;
@@ -157,8 +156,6 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     sch->n_multi = tot[0];
     sch->counter_s[0] = 0;
     sch->counter_s[1] = 0;
-    sch->done[0] = 0;
-    sch->done[1] = 0;
   }
 }
 
@@ -495,8 +492,6 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
       int ti = -1, n0 = 0, nb = 0;
       if (it < D.total) {
         D.decode(it, &ti, &n0, &nb);
-      } else {
-        queue_release(a.counter, a.counter_s, a.done);
       }
       next_item[0] = ti;
       next_item[1] = n0;
@@ -599,7 +594,6 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.d;
     g.counter = &L.sch->counter[0];
     g.counter_s = &L.sch->counter_s[0];
-    g.done = &L.sch->done[0];
     g.wr = item_weight_rows(L, L.f, 2);
     g.nb = 1;
     g.nb_skinny = 1;
@@ -615,7 +609,6 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.K = L.f;
     g.counter = &L.sch->counter[1];
     g.counter_s = &L.sch->counter_s[1];
-    g.done = &L.sch->done[1];
     g.wr = item_weight_rows(L, L.d, 1);
     g.nb = item_blocks(g.wr, L.d, 1, 2);
     g.nb_skinny = item_blocks(g.wr, L.d, 1, 4);
