@@ -271,15 +271,27 @@ def device_bytes_needed(wl):
     return int(b * 1.1)
 
 
-def measure(name, args, dev, owner_arg=None, cpu_seconds=None):
+def chunk_workload(name, tokens):
+    """The named workload's shapes and input recipe with only `tokens` tokens
+    (a decode-sized chunk), under a name of its own."""
+    from routed_expert_prefill_amd import synth
+
+    base = synth.WORKLOADS[name]
+    return base.replace(T=tokens, name=f"chunk_T{tokens}_d{base.d}_f{base.f}_E{base.E}_"
+                                       f"{base.routing}_{base.dtype}")
+
+
+def measure(name, args, dev, owner_arg=None, cpu_seconds=None, tokens=None):
     """One workload: warm-up, K timed steps, a second per-call pass, the
-    dominant kernel's roofline, and (optionally) the CPU oracle's sample."""
+    dominant kernel's roofline, and (optionally) the CPU oracle's sample.
+    With tokens, the workload's first-`tokens` chunk (chunk_workload)."""
     import torch
 
     import routed_expert_prefill_amd as rep
     from routed_expert_prefill_amd import synth
 
-    wl = synth.WORKLOADS[name]
+    wl = synth.WORKLOADS[name] if tokens is None else chunk_workload(name, tokens)
+    name = wl.name
     fp8 = wl.dtype == "fp8"
     free, total = torch.cuda.mem_get_info(dev)
     need = device_bytes_needed(wl)
@@ -359,7 +371,8 @@ def measure(name, args, dev, owner_arg=None, cpu_seconds=None):
         pk = MFMA_PEAK_TFLOPS[wl.dtype]
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(ach / pk, 4)}
-    roof["traffic"] = traffic_from_profiles(name) if owner is None else None
+    roof["traffic"] = (traffic_from_profiles(name) if owner is None and tokens is None
+                       else None)
     roof["kernel"] = ("grouped_gemm8_kernel<true>" if fp8 else "grouped_gemm_kernel<true>") + \
         " (gate/up GEMM, SwiGLU epilogue)"
     roof["avg_ms"] = round(gu_avg, 5)
@@ -445,6 +458,9 @@ def main():
     ap.add_argument("--owner", default=None, metavar="G:g",
                     help="measure one owner's share: experts split into G contiguous ranges, "
                          "only routes to range g stay active (the sharded layout on one GPU)")
+    ap.add_argument("--tokens", type=int, default=None, metavar="N",
+                    help="measure a chunk of N tokens with the workload's shapes and input "
+                         "recipe (decode-sized chunks); no sub-records")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 1 GiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -477,10 +493,12 @@ def main():
         del src, dst
 
     head = measure(name, args, dev, owner_arg=args.owner,
-                   cpu_seconds=None if args.no_cpu_baseline else args.cpu_seconds)
-    router = router_timing(name, dev)
+                   cpu_seconds=None if args.no_cpu_baseline else args.cpu_seconds,
+                   tokens=args.tokens)
+    router = router_timing(name, dev) if args.tokens is None else None
     subs = []
-    if args.workload is None and args.owner is None and not args.no_sub_records:
+    if (args.workload is None and args.owner is None and args.tokens is None
+            and not args.no_sub_records):
         for sub in SUB_WORKLOADS:
             rec = measure(sub, args, dev,
                           cpu_seconds=None if args.no_cpu_baseline else args.sub_cpu_seconds)

@@ -62,6 +62,7 @@ struct GgArgs {
   const int *n_small;  // 32-row tiles at the end of the tile list
   const int *n_multi;  // tiles of experts with several tiles, at the start of the list
   int *counter_s;      // head of the second queue (items of the other tiles)
+  int static_items;    // 1: workgroup b takes items b, b + grid, ... (no queue)
 };
 
 constexpr int kGgThreads = 512;
@@ -81,20 +82,16 @@ struct GgRing {
 
 constexpr int kGsThreads = 256;
 
-__device__ int gs_scan(int v, int *total, int *buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kGsThreads; off <<= 1) {
-    const int x = (t >= off) ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += x;
-    __syncthreads();
+constexpr int kGsWaves = kGsThreads / kWave;
+
+// Inclusive sum of v over the lanes of a wave up to this one.
+__device__ __forceinline__ int gs_wave_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int x = __shfl_up(v, off, kWave);
+    if (lane >= off) v += x;
   }
-  const int incl = buf[t];
-  *total = buf[kGsThreads - 1];
-  __syncthreads();
-  return incl - v;
+  return v;
 }
 
 // One thread per expert: full 256-row tiles, then one remainder tile whose
@@ -102,7 +99,8 @@ __device__ int gs_scan(int v, int *total, int *buf) {
 // written tallest class first.
 __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
     const int32_t *__restrict__ offsets, int E, Schedule *sch, Tile *__restrict__ tiles) {
-  __shared__ int buf[kGsThreads];
+  constexpr int NC = 6;
+  __shared__ int wave_tot[kGsWaves][NC];
   const int e = threadIdx.x;
   int n = 0, row0 = 0;
   if (e < E) {
@@ -119,12 +117,28 @@ __global__ __launch_bounds__(kGsThreads) void grouped_schedule_kernel(
                                  : 8;
   // classes, tallest first: ablk 8 of experts with several tiles, ablk 8 of
   // single-tile experts, then 6, 4, 2, 1
-  constexpr int NC = 6;
   const int n8 = nfull + (rab == 8);
   const bool multi = n > kTileRows;
   int cnt[NC] = {multi ? n8 : 0, multi ? 0 : n8, rab == 6, rab == 4, rab == 2, rab == 1};
+  // per class: exclusive prefix over the experts (wave scans, then the
+  // totals of the waves before this one) and the total over all experts
   int pos[NC], tot[NC];
-  for (int c = 0; c < NC; ++c) pos[c] = gs_scan(cnt[c], &tot[c], buf);
+  const int wave = threadIdx.x / kWave;
+  for (int c = 0; c < NC; ++c) {
+    pos[c] = gs_wave_scan(cnt[c]);
+    if ((threadIdx.x & (kWave - 1)) == kWave - 1) wave_tot[wave][c] = pos[c];
+  }
+  __syncthreads();
+  for (int c = 0; c < NC; ++c) {
+    int before = 0, all = 0;
+    for (int w = 0; w < kGsWaves; ++w) {
+      const int v = wave_tot[w][c];
+      before += w < wave ? v : 0;
+      all += v;
+    }
+    pos[c] += before - cnt[c];
+    tot[c] = all;
+  }
   int base = 0;
   for (int c = 0; c < NC; ++c) {
     pos[c] += base;
@@ -486,9 +500,16 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
   // monotonic, so tuned to this workload); 401 and 2048 tokens unchanged.
   const GgDispatch<GATEUP> D(a);
   TwoQueue queue(vreg(*a.n_multi) * D.ptb, D.total, GATEUP ? MOE_SSW4_GU : MOE_SSW4_DN, D.grid);
+  int next_static = vreg((int)blockIdx.x);
   for (;;) {
     if (threadIdx.x == 0) {
-      const int it = queue.next(a.counter, a.counter_s);
+      int it;
+      if (a.static_items) {
+        it = min(next_static, D.total);
+        next_static += D.grid;
+      } else {
+        it = queue.next(a.counter, a.counter_s);
+      }
       int ti = -1, n0 = 0, nb = 0;
       if (it < D.total) {
         D.decode(it, &ti, &n0, &nb);
@@ -565,6 +586,12 @@ static int item_weight_rows(const FfnLaunch &L, int n_out, int mats) {
   return best;
 }
 
+// With at most 32 routed rows every tile is a 32-row tile and every item
+// streams the same weight bytes, so a fixed assignment (item b, b + grid,
+// ... to workgroup b) balances as well as the work queues and saves their
+// atomics at the start and end of every workgroup.
+static int static_items(const FfnLaunch &L) { return L.R <= 32 ? 1 : 0; }
+
 // Feature blocks per item: more than one only for full-width items (narrow
 // items exist to make more of them) and when the blocks tile the output
 // features exactly.
@@ -597,6 +624,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.wr = item_weight_rows(L, L.f, 2);
     g.nb = 1;
     g.nb_skinny = 1;
+    g.static_items = static_items(L);
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(L.num_cus), dim3(kGgThreads), 0, stream, g);
   }
   if (stages & kStageDown) {
@@ -612,6 +640,7 @@ hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t s
     g.wr = item_weight_rows(L, L.d, 1);
     g.nb = item_blocks(g.wr, L.d, 1, 2);
     g.nb_skinny = item_blocks(g.wr, L.d, 1, 4);
+    g.static_items = static_items(L);
     hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(L.num_cus), dim3(kGgThreads), 0, stream,
                        g);
   }
