@@ -56,7 +56,8 @@ struct GgArgs {
   const Tile *tiles;
   const int *ntiles;
   int *counter;        // compute-queue head (TwoQueue), zeroed by the schedule
-  int wr;              // weight rows per item: 256, or 128 / 64 when every tile holds <= 32 rows
+  int wr;              // weight rows per item: 256, 128 or 64 (at most 32 routed rows), or 0:
+                       // 128 if every tile is a 32-row tile, else 256 (decided on the device)
   int nb;              // feature blocks per item (streamed through one ring fill)
   int nb_skinny;       // the same for 32-row tiles when nearly all tiles are 32-row ones
   const int *n_small;  // 32-row tiles at the end of the tile list
@@ -416,71 +417,94 @@ __device__ __forceinline__ void gg_item_any(const GgArgs &a, const Tile &t, int 
 // registers while the workgroup multiplies, and only thread 0 decodes items.
 template <bool GATEUP>
 struct GgDispatch {
-  int nbig, nsm, ptb, pts, pt1, FEAT, FIB, FIS, nbb, nbs, items_big, items_mid, total, N, grid;
+  int nbig, nsm, ptb, pts, ptt, FEATB, FEATS, FIB, FIS, nbb, nbs, items_big, items_mid, total, N,
+      grid, wrb, wrs;
   __device__ __forceinline__ explicit GgDispatch(const GgArgs &a) {
     N = vreg(a.N);
     grid = vreg((int)gridDim.x);
+    const int nsmall = vreg(*a.n_small);
+    nbig = vreg(*a.ntiles) - nsmall;
+    // weight rows per item of the taller tiles (wrb) and of the 32-row tiles
+    // (wrs).  Left to the device (0), 32-row tiles take 128-row items when
+    // there are no taller tiles: on MI355X at 401 tokens (every expert under
+    // 32 rows) gate/up 1.349 -> 1.313 ms and down 0.703 -> 0.687 ms, one
+    // expert owner's share 0.348 -> 0.320 ms per step: twice the items to
+    // balance, and a 20 KB stage leaves eight ring slots where a 36 KB one
+    // leaves four.
     const int wr = vreg(a.wr);
-    // output features per item: half the weight rows for gate/up (gate and up
-    // rows of the same features), all of them for down
-    FEAT = GATEUP ? wr / 2 : wr;
+    // (also narrowing the 32-row tiles of mixed lists: 2048 tokens -1%,
+    // 8192 Zipf-routed tokens +4%, so not done)
+    const bool narrow = wr == 0 && nbig == 0;
+    wrb = wr == 0 ? kGgWRows : wr;
+    wrs = narrow ? kGgWRows / 2 : wrb;
+    // output features per block: half the weight rows for gate/up (gate and
+    // up rows of the same features), all of them for down
+    FEATB = GATEUP ? wrb / 2 : wrb;
+    FEATS = GATEUP ? wrs / 2 : wrs;
     // items of taller tiles first (the list is tallest first), then of the
     // 32-row tiles; the 32-row tiles take nb_skinny blocks per item when the
     // taller ones are at most an eighth as many (on MI355X, 4 blocks were
-    // best there and 2 elsewhere, for 200 to 8192 tokens)
-    const int nsmall = vreg(*a.n_small);
-    nbig = vreg(*a.ntiles) - nsmall;
+    // best there and 2 elsewhere, for 200 to 8192 tokens; narrowed items take
+    // one block)
     const bool skinny = nbig * 8 <= nsmall;
     nbb = vreg(a.nb);
-    nbs = skinny ? vreg(a.nb_skinny) : nbb;
+    nbs = narrow ? 1 : skinny ? vreg(a.nb_skinny) : nbb;
     // with few tiles, halve the blocks per item until at least half the
     // workgroups have an item: a workgroup of a half-idle chip streams faster
     // than its even share, so long items on half of them still pay (measured:
     // 11 experts 0.175 -> 0.123 ms with the halving, 43 experts 4% slower if
     // every workgroup had to get one).  Block counts above one divide the
     // feature blocks of a tile.
-    pt1 = (N + FEAT - 1) / FEAT;
-    while ((nbb > 1 || nbs > 1) && 2 * (nbig * (pt1 / nbb) + nsmall * (pt1 / nbs)) < grid) {
+    const int ptb1 = (N + FEATB - 1) / FEATB;
+    ptt = (N + FEATS - 1) / FEATS;  // one-block items of a 32-row tile
+    while ((nbb > 1 || nbs > 1) && 2 * (nbig * (ptb1 / nbb) + nsmall * (ptt / nbs)) < grid) {
       if (nbs >= nbb)
         nbs >>= 1;
       else
         nbb >>= 1;
     }
-    FIB = FEAT * nbb;  // output features per item
-    FIS = FEAT * nbs;
+    FIB = FEATB * nbb;  // output features per item
+    FIS = FEATS * nbs;
     ptb = (N + FIB - 1) / FIB;
     pts = (N + FIS - 1) / FIS;
     // when (nearly) all tiles are 32-row ones, the last of them (about two
     // rounds of items) go out one block per item, so that the end of the
     // queue balances at a fine grain (MI355X: down 0.725 -> 0.705 ms at 401
     // tokens, -3% at 200 and 1024; with many taller tiles it did not help)
-    const int ntail = (skinny && nbs > 1) ? min(nsmall, (2 * grid + pt1 - 1) / pt1) : 0;
+    const int ntail = (skinny && nbs > 1) ? min(nsmall, (2 * grid + ptt - 1) / ptt) : 0;
     nsm = nsmall - ntail;
     items_big = nbig * ptb;
     items_mid = items_big + nsm * pts;
-    total = items_mid + ntail * pt1;
+    total = items_mid + ntail * ptt;
   }
-  // tile index, first output feature and feature blocks of item it
-  __device__ __forceinline__ void decode(int it, int *ti, int *n0, int *nb) const {
-    int nbw;
+  // tile index, first output feature, feature blocks and weight rows per
+  // block of item it
+  __device__ __forceinline__ void decode(int it, int *ti, int *n0, int *nb, int *wr) const {
+    int nbw, feat;
     if (it < items_big) {
       *ti = it / ptb;
       *n0 = (it - *ti * ptb) * FIB;
       nbw = nbb;
+      feat = FEATB;
+      *wr = wrb;
     } else if (it < items_mid) {
       const int is = it - items_big;
       const int q = is / pts;
       *ti = nbig + q;
       *n0 = (is - q * pts) * FIS;
       nbw = nbs;
+      feat = FEATS;
+      *wr = wrs;
     } else {
       const int is = it - items_mid;
-      const int q = is / pt1;
+      const int q = is / ptt;
       *ti = nbig + nsm + q;
-      *n0 = (is - q * pt1) * FEAT;
+      *n0 = (is - q * ptt) * FEATS;
       nbw = 1;
+      feat = FEATS;
+      *wr = wrs;
     }
-    *nb = min(nbw, (N - *n0 + FEAT - 1) / FEAT);
+    *nb = min(nbw, (N - *n0 + feat - 1) / feat);
   }
 };
 
@@ -510,14 +534,15 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
       } else {
         it = queue.next(a.counter, a.counter_s);
       }
-      int ti = -1, n0 = 0, nb = 0;
+      int ti = -1, n0 = 0, nb = 0, wr = 0;
       if (it < D.total) {
-        D.decode(it, &ti, &n0, &nb);
+        D.decode(it, &ti, &n0, &nb, &wr);
       }
       next_item[0] = ti;
       next_item[1] = n0;
       next_item[2] = nb;
       next_item[3] = a.K;
+      next_item[4] = wr;
     }
     __syncthreads();
     // read before gg_item's first barrier (its loads overwrite it); uniform,
@@ -531,10 +556,11 @@ __global__ __launch_bounds__(kGgThreads, 1) void grouped_gemm_kernel(GgArgs a) {
     const int nb = __builtin_amdgcn_readfirstlane(next_item[2]);
     GgArgs ai = a;
     ai.K = __builtin_amdgcn_readfirstlane(next_item[3]);
+    const int wr = __builtin_amdgcn_readfirstlane(next_item[4]);
     const Tile t = a.tiles[ti];
-    if (a.wr == 128) {
+    if (wr == 128) {
       gg_item_any<GATEUP, 1, 128>(ai, t, n0, nb, ring, ring_lds);
-    } else if (a.wr == 64) {
+    } else if (wr == 64) {
       gg_item_any<GATEUP, 1, 64>(ai, t, n0, nb, ring, ring_lds);
     } else {
       switch (tile_class(t)) {
@@ -566,10 +592,11 @@ hipError_t launch_grouped_schedule(const int32_t *offsets, int E, Schedule *sch,
 // minimises (rounds of items over the CUs) x (weight rows per item + 32),
 // counting at most min(R, E) tiles; the 32 rows stand for an item's fixed
 // cost (ring fill and queue round trip, ~4 us, measured) and ties go to the
-// wider item.  n_out: output features of the projection; mats: weight
-// matrices interleaved in an item (2 for gate/up).
+// wider item.  With more rows the kernel chooses (0 here): 128 when every
+// tile is a 32-row tile, else 256.  n_out: output features of the
+// projection; mats: weight matrices interleaved in an item (2 for gate/up).
 static int item_weight_rows(const FfnLaunch &L, int n_out, int mats) {
-  if (L.R > 32) return kGgWRows;
+  if (L.R > 32) return 0;  // the kernel decides from the tile list
   const long long tiles = L.R < L.E ? L.R : L.E;
   const int cus = L.num_cus > 0 ? L.num_cus : 1;
   int best = kGgWRows;
@@ -596,6 +623,7 @@ static int static_items(const FfnLaunch &L) { return L.R <= 32 ? 1 : 0; }
 // items exist to make more of them) and when the blocks tile the output
 // features exactly.
 static int item_blocks(int wr, int n_out, int mats, int want) {
+  if (wr == 0) wr = kGgWRows;  // the blocks of full-width items (narrowed ones take one)
   const int feat = wr / mats;
   return (want > 1 && wr == kGgWRows && n_out % (feat * want) == 0) ? want : 1;
 }
