@@ -9,7 +9,10 @@
 //
 // Rows of up to 4096 elements: one wave per row; longer rows (up to
 // kQMaxCols): one workgroup per row.  Either way a row is read once into
-// registers, reduced, then encoded and written.
+// registers, reduced, then encoded and written; the quotients are formed by
+// a reciprocal multiply where that provably gives the same code and encoded
+// by the conversion instruction (quant_e4m3_x4), by IEEE division and the
+// bit-level encoder elsewhere.
 #include "kernels.h"
 
 namespace moe {
@@ -30,6 +33,73 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   // subnormal range: multiples of 2^-9 (8 * 2^-9 = 2^-6 encodes as 0x08)
   const float s = __uint_as_float(a) * 512.0f;
   return sign | (uint32_t)__builtin_rintf(s);
+}
+
+// E4M3 codes of two fp32 values that are not NaN, in bytes 2 HI and 2 HI + 1
+// of old: gfx950's conversion instruction (OCP E4M3FN, round to nearest
+// even) on the values clamped to +-448.  On every fp32 pattern of magnitude
+// below 464 it gives the same code as f32_to_e4m3 (subnormal codes and ties
+// included; checked on MI355X), and from 464 on NaN, hence the clamp.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_e4m3_x2(float a, float b, uint32_t old) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// q = e4m3_rne_saturate(fl32(v / sc)) without a division for nearly every
+// element.  rcp = fl32(1 / sc); exact: the row needs the division throughout
+// (sc not a normal float, or rcp not finite).
+//
+// y = v * rcp differs from fl32(v / sc) by a few units in the last place
+// (two roundings of relative size 2^-24 each against one), i.e. by at most a
+// handful of consecutive fp32 bit patterns.  E4M3 rounding is monotone and
+// changes only at the midpoints between neighbouring codes, which in the
+// normal range are the patterns whose low 20 bits are 0x80000.  So where y
+// lies in the normal range and more than 16 patterns from a midpoint, the
+// quotient has y's code.  Within that window (ties included), in the
+// subnormal-code range, for NaN and for rows flagged exact the quotient is
+// formed by IEEE division instead; the flag costs three compares, and the
+// division runs behind one branch for the rare flagged elements.
+__device__ __forceinline__ bool quant_needs_division(float y) {
+  const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
+  return (a - 1u) < 0x3c7fffffu           // 0 < |y| < 2^-6: subnormal codes
+         || a > 0x7f800000u               // NaN
+         || ((a & 0xfffffu) - 0x7fff0u) < 32u;  // near a midpoint
+}
+
+// Four codes (one byte each) for the bf16 pairs lo and hi.  zero: the row is
+// all zeros and every code is 0.
+__device__ __forceinline__ uint32_t quant_e4m3_x4(uint32_t lo, uint32_t hi, float sc, float rcp,
+                                                  bool exact, bool zero) {
+  float v[4], y[4];
+  v[0] = bf16_bits_to_f32((uint16_t)(lo & 0xffffu));
+  v[1] = bf16_bits_to_f32((uint16_t)(lo >> 16));
+  v[2] = bf16_bits_to_f32((uint16_t)(hi & 0xffffu));
+  v[3] = bf16_bits_to_f32((uint16_t)(hi >> 16));
+  bool any = exact;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[e] = v[e] * rcp;
+    any = any || quant_needs_division(y[e]);
+  }
+  uint32_t packed = cvt_e4m3_x2<false>(y[0], y[1], 0u);
+  packed = cvt_e4m3_x2<true>(y[2], y[3], packed);
+  if (any) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (exact || quant_needs_division(y[e]))
+        packed = (packed & ~(0xffu << (8 * e))) | (f32_to_e4m3(v[e] / sc) << (8 * e));
+    }
+  }
+  return zero ? 0u : packed;
+}
+
+// The reciprocal of a row scale, and whether the row must divide throughout.
+__device__ __forceinline__ float quant_rcp(float sc, bool *exact) {
+  const float r = 1.0f / sc;
+  *exact = !(sc >= 1.17549435e-38f) || !(r < 3.40282347e38f);  // sc subnormal, r overflowed
+  return r;
 }
 
 constexpr int kQThreads = 256;
@@ -76,6 +146,8 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
     __syncthreads();
     const bool zero = amax == 0.0f;
     const float sc = zero ? 1.0f : amax / 448.0f;
+    bool exact;
+    const float rcp = quant_rcp(sc, &exact);
     if (tid == 0) s[row] = sc;
     uint8_t *dst = q + (size_t)row * cols;
 #pragma unroll
@@ -86,17 +158,10 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int w = 0; w < 4; w += 2) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t two = (uint32_t)raw[p][h][w + (e >> 1)];
-              const uint16_t bits = (e & 1) ? (uint16_t)(two >> 16) : (uint16_t)(two & 0xffffu);
-              const uint32_t code = zero ? 0u : f32_to_e4m3(bf16_bits_to_f32(bits) / sc);
-              packed |= code << (8 * e);
-            }
-            out[h * 2 + (w >> 1)] = (int)packed;
-          }
+          for (int w = 0; w < 4; w += 2)
+            out[h * 2 + (w >> 1)] = (int)quant_e4m3_x4((uint32_t)raw[p][h][w],
+                                                       (uint32_t)raw[p][h][w + 1], sc, rcp, exact,
+                                                       zero);
         *reinterpret_cast<i32x4 *>(dst + c) = out;
       }
     }
@@ -104,11 +169,11 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
 }
 
 // Rows of at most kQWaveMaxCols elements: one wave per row (four rows per
-// workgroup), lane l holding elements 8 l + 512 i .. +7, the row maximum
-// reduced with shuffles only.  Same arithmetic as quant_rows_kernel.
+// workgroup), lane l holding elements 8 l + 512 i .. +7 for i < NL, the row
+// maximum reduced with shuffles only.  Same arithmetic as quant_rows_kernel.
 constexpr int kQWaveMaxCols = 4096;
-constexpr int kQWaveLoads = kQWaveMaxCols / (kWave * 8);  // 16-byte loads per lane
 
+template <int NL>
 __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
     const uint16_t *__restrict__ x, int rows, const int32_t *rows_dev, int cols,
     uint8_t *__restrict__ q, float *__restrict__ s) {
@@ -117,13 +182,17 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
   const int waves = gridDim.x * (kQThreads / kWave);
   for (int row = blockIdx.x * (kQThreads / kWave) + threadIdx.x / kWave; row < nrows; row += waves) {
     const uint16_t *src = x + (size_t)row * cols;
-    i32x4 raw[kQWaveLoads];
+    i32x4 raw[NL];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kQWaveLoads; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const int c = (i * kWave + lane) * 8;  // cols is a multiple of 8
+      if (c < cols) raw[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + c));
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = (i * kWave + lane) * 8;
       if (c < cols) {
-        raw[i] = *reinterpret_cast<const i32x4 *>(src + c);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t two = (uint32_t)raw[i][w];
@@ -135,25 +204,17 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
     for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const bool zero = amax == 0.0f;
     const float sc = zero ? 1.0f : amax / 448.0f;
+    bool exact;
+    const float rcp = quant_rcp(sc, &exact);
     if (lane == 0) s[row] = sc;
     uint8_t *dst = q + (size_t)row * cols;
 #pragma unroll
-    for (int i = 0; i < kQWaveLoads; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const int c = (i * kWave + lane) * 8;
       if (c < cols) {
         uint2 out;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t two = (uint32_t)raw[i][h * 2 + (e >> 1)];
-            const uint16_t bits = (e & 1) ? (uint16_t)(two >> 16) : (uint16_t)(two & 0xffffu);
-            const uint32_t code = zero ? 0u : f32_to_e4m3(bf16_bits_to_f32(bits) / sc);
-            packed |= code << (8 * e);
-          }
-          (h ? out.y : out.x) = packed;
-        }
+        out.x = quant_e4m3_x4((uint32_t)raw[i][0], (uint32_t)raw[i][1], sc, rcp, exact, zero);
+        out.y = quant_e4m3_x4((uint32_t)raw[i][2], (uint32_t)raw[i][3], sc, rcp, exact, zero);
         *reinterpret_cast<uint2 *>(dst + c) = out;
       }
     }
@@ -167,9 +228,20 @@ hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_de
   if (cols <= kQWaveMaxCols) {
     const int per_block = kQThreads / kWave;
     const long long want = ((long long)rows + per_block - 1) / per_block;
-    const int grid = (int)(want < grid_cap ? want : grid_cap);
-    hipLaunchKernelGGL(quant_rows_wave_kernel, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
-                       stream, x, rows, rows_dev, cols, q, s);
+    // up to 16 workgroups per CU (four times grid_cap): more rows in flight
+    // at once (MI355X, 46,700 x 2048: 4 per CU 106 us, 16 per CU 80 us)
+    const long long cap = (long long)grid_cap * 4;
+    const int grid = (int)(want < cap ? want : cap);
+    const int nl = (cols + kWave * 8 - 1) / (kWave * 8);
+    if (nl <= 2)
+      hipLaunchKernelGGL(quant_rows_wave_kernel<2>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+                         stream, x, rows, rows_dev, cols, q, s);
+    else if (nl <= 4)
+      hipLaunchKernelGGL(quant_rows_wave_kernel<4>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+                         stream, x, rows, rows_dev, cols, q, s);
+    else
+      hipLaunchKernelGGL(quant_rows_wave_kernel<8>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+                         stream, x, rows, rows_dev, cols, q, s);
     return hipGetLastError();
   }
   const int grid = rows < grid_cap ? rows : grid_cap;

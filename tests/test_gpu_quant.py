@@ -71,3 +71,23 @@ def test_zero_rows_and_wide_dynamic_range():
     qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
     assert np.array_equal(q, qr) and np.array_equal(s, sr)
     assert s[1] == 1.0 and not q[1].any() and not q[2].any()
+
+
+def test_every_bf16_value_with_unit_scale():
+    """Rows whose largest magnitude is 448 have scale 1, so every quotient is
+    the bf16 value itself: all finite bf16 patterns of magnitude at most 448,
+    both signs, against the oracle's encoder (every E4M3 code, every tie,
+    the subnormal codes)."""
+    mags = np.arange(0, 0x43e0 + 1, dtype=np.uint16)  # +0 .. 448 as bf16 bit patterns
+    vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+    cols = 4096
+    per_row = cols - 1
+    nrows = -(-len(vals) // per_row)
+    bits = np.zeros((nrows, cols), np.uint16)
+    bits[:, 0] = 0x43e0  # 448
+    flat = np.resize(vals, nrows * per_row)  # the last row repeats values from the start
+    bits[:, 1:] = flat.reshape(nrows, per_row)
+    q, s = _gpu(bits)
+    qr, sr = nx.quant_rows_fp8(nx.bf16_bits_to_f64(bits).astype(np.float32))
+    assert np.all(s == 1.0) and np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
