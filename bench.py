@@ -323,6 +323,23 @@ def measure(name, args, dev, owner_arg=None, cpu_seconds=None, tokens=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    graph = None
+    if args.graph:
+        # one step captured in a HIP graph (after a pass on the capture
+        # stream) and replayed in the timed region: no host launch cost
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize(dev)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -330,13 +347,17 @@ def measure(name, args, dev, owner_arg=None, cpu_seconds=None, tokens=None):
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step(evs[i])
     end.record(stream)
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
-    gu_ms = [a.elapsed_time(b) for a, b in evs]
-    gu_avg = sum(gu_ms) / len(gu_ms)
+    if graph is None:
+        gu_ms = [a.elapsed_time(b) for a, b in evs]
+        gu_avg = sum(gu_ms) / len(gu_ms)
 
     # each call timed alone: a second pass of K steps (after the timed
     # region) with events between the calls; per-step median/MAD/min from it
@@ -352,6 +373,9 @@ def measure(name, args, dev, owner_arg=None, cpu_seconds=None, tokens=None):
                   "mad": round(med([abs(v - step_med) for v in per_step]), 5),
                   "min": round(min(per_step), 5)}
     stages_ms = {n: round(med(v), 5) for n, v in per_stage.items()}
+    if graph is not None:  # gate/up timed in the per-call pass (events cannot sit in the replays)
+        gu_avg = sum(per_stage["gate_up"]) / len(per_stage["gate_up"])
+        del graph
     log(f"{name}: {ms_step:.4f} ms/step (wall {1e3 * t_wall / args.steps:.4f}); "
         f"per step median {step_stats['median']:.4f} ms; stages {stages_ms}")
 
@@ -397,7 +421,8 @@ def measure(name, args, dev, owner_arg=None, cpu_seconds=None, tokens=None):
         "dtype": wl.dtype,
         "config": {"workload": name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
                    "routing": wl.routing, "mask_p": wl.mask_p, "weights": wl.dtype,
-                   "parallelism": "single-gpu" if owner is None else f"expert owner {owner}"},
+                   "parallelism": "single-gpu" if owner is None else f"expert owner {owner}",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "path": {"tflops": round(work["path_flops"] / (ms_step / 1e3) / 1e12, 2),
                  "algorithmic_gb": round(work["path_bytes"] / 1e9, 3),
                  "hbm_gbs": round(work["path_bytes"] / (ms_step / 1e3) / 1e9, 1),
@@ -461,6 +486,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, metavar="N",
                     help="measure a chunk of N tokens with the workload's shapes and input "
                          "recipe (decode-sized chunks); no sub-records")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (no host launch "
+                         "cost: for decode-sized chunks); gate/up is then timed in the per-call pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device-to-device copy of 1 GiB (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
