@@ -449,6 +449,12 @@ struct GgDispatch {
     const bool skinny = nbig * 8 <= nsmall;
     nbb = vreg(a.nb);
     nbs = narrow ? 1 : skinny ? vreg(a.nb_skinny) : nbb;
+    // narrowed down items take four blocks while the 32-row tiles are fewer
+    // than the workgroups (MI355X: one expert owner's share, 32 tiles, down
+    // 0.106 -> 0.102 ms; 16 tokens 0.636 -> 0.619 ms, 32 tokens 1.054 ->
+    // 1.037 ms per step); with a tile per workgroup or more one block is
+    // best (401 tokens, 256 tiles: down 0.689 ms, 0.715 with two, 0.699 with four)
+    if (narrow && !GATEUP && nsmall < grid && N % (4 * FEATS) == 0) nbs = 4;
     // with few tiles, halve the blocks per item until at least half the
     // workgroups have an item: a workgroup of a half-idle chip streams faster
     // than its even share, so long items on half of them still pay (measured:
