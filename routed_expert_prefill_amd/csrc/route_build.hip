@@ -2,12 +2,15 @@
 // ("perf(ds4): batch heterogeneous MoE prefill by expert", Summary).
 //
 // Up to 6144 routes: one workgroup does all three steps (rb_fused_kernel).
-// Beyond that, three launches over chunks of kChunk routes:
+// Beyond that, two launches over chunks of kChunk routes:
 //   1. per-chunk histogram in LDS (integer atomics: order-independent);
-//   2. one workgroup scans the chunk histograms per bin and the bin totals;
-//   3. per-chunk stable scatter: each wave walks its routes 64 at a time in
-//      route order, finds equal keys among the 64 lanes with one ballot per
-//      key bit, and ranks each lane among its earlier peers.
+//   2. per-chunk stable scatter.  Each workgroup first forms, from all the
+//      chunk histograms, the bin totals, their exclusive prefix (the
+//      offsets) and the counts of its bins in the chunks before its own, so
+//      no launch between the two scans the histograms; then each wave walks
+//      its routes 64 at a time in route order, finds equal keys among the 64
+//      lanes with one ballot per key bit, and ranks each lane among its
+//      earlier peers.
 // Results are integers and do not depend on scheduling.
 #include <mutex>
 
@@ -19,9 +22,10 @@ constexpr int kRbThreads = 256;
 constexpr int kRbWaves = kRbThreads / kWave;
 // Measured on MI355X (route build alone, uniform routing over 256 experts):
 // the one-workgroup path takes 11 us up to ~4k routes, 14 us at 6,144,
-// 19 us at 8,196 and 25 us at 12,288; the three launches take 16.4-17 us
-// from 8k to 49k routes (1,024-route chunks ~1 us faster than 2,048 at
-// 49k, 512-route chunks 4 us slower).
+// 19 us at 8,196 and 25 us at 12,288; the chunked path (then three
+// launches, a one-workgroup scan between histogram and scatter) took
+// 16.4-17 us from 8k to 49k routes (1,024-route chunks ~1 us faster than
+// 2,048 at 49k, 512-route chunks 4 us slower).
 #ifndef MOE_RB_CHUNK
 #define MOE_RB_CHUNK 1024
 #endif
@@ -53,68 +57,84 @@ __global__ __launch_bounds__(kRbThreads) void rb_hist_kernel(const int32_t *__re
   for (int b = threadIdx.x; b <= E; b += kRbThreads) chunk_hist[(size_t)blockIdx.x * (E + 1) + b] = h[b];
 }
 
-// One workgroup of 512 threads: bin b's chunk prefix, bin totals, offsets.
-constexpr int kScanThreads = 512;
-
-__global__ __launch_bounds__(kScanThreads) void rb_scan_kernel(const int32_t *__restrict__ chunk_hist,
-                                                               int nchunks, int E,
-                                                               int32_t *__restrict__ counts,
-                                                               int32_t *__restrict__ offsets,
-                                                               int32_t *__restrict__ chunk_base) {
-  __shared__ int tot[kScanThreads];
-  const int b = threadIdx.x;
-  int s = 0;
-  // eight chunks at a time: their counts are loaded together, so a bin
-  // costs one memory round trip per eight chunks rather than per chunk
-  constexpr int U = 8;
-  if (b <= E) {
-    for (int c0 = 0; c0 < nchunks; c0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[u] = c0 + u < nchunks ? chunk_hist[(size_t)(c0 + u) * (E + 1) + b] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c0 + u < nchunks) chunk_base[(size_t)(c0 + u) * (E + 1) + b] = s;
-        s += v[u];
-      }
-    }
-    counts[b] = s;
+// Exclusive prefix of v over the threads of the workgroup; *total = the sum.
+__device__ __forceinline__ int rb_block_scan(int v, int *total, int *wave_sums) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int x = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
   }
-  tot[b] = (b <= E) ? s : 0;
+  if (lane == kWave - 1) wave_sums[w] = x;
   __syncthreads();
-  // inclusive Hillis-Steele scan over the bins
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = (b >= off) ? tot[b - off] : 0;
-    __syncthreads();
-    tot[b] += v;
-    __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < kRbWaves; ++i) {
+    const int s = wave_sums[i];
+    before += i < w ? s : 0;
+    all += s;
   }
-  const int excl = (b == 0) ? 0 : tot[b - 1];
-  if (b <= E + 1) offsets[b] = excl;
-  if (b <= E) {
-    for (int c0 = 0; c0 < nchunks; c0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[u] = c0 + u < nchunks ? chunk_base[(size_t)(c0 + u) * (E + 1) + b] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (c0 + u < nchunks) chunk_base[(size_t)(c0 + u) * (E + 1) + b] = v[u] + excl;
-    }
-  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
 }
 
 __global__ __launch_bounds__(kRbThreads) void rb_scatter_kernel(const int32_t *__restrict__ ids,
                                                                 const uint8_t *__restrict__ mask,
                                                                 int R, int E, int key_bits,
-                                                                const int32_t *__restrict__ chunk_base,
+                                                                int nchunks,
+                                                                const int32_t *__restrict__ chunk_hist,
+                                                                int32_t *__restrict__ counts,
+                                                                int32_t *__restrict__ offsets,
                                                                 int32_t *__restrict__ sorted_routes,
                                                                 int32_t *__restrict__ route_rows) {
   __shared__ int cnt[kRbWaves][kMaxBins];
+  __shared__ int chunk_start[kMaxBins];  // bin b's first row for this chunk
+  __shared__ int wave_sums[kRbWaves];
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
   for (int i = threadIdx.x; i < kRbWaves * kMaxBins; i += kRbThreads) (&cnt[0][0])[i] = 0;
+
+  // bin totals over all chunks and the counts in the chunks before this
+  // one; thread t holds bins t and (for E = 256) t + 256, and the exclusive
+  // prefix of the totals is one scan over the threads of their pairs' sums
+  int tot[2] = {0, 0}, before[2] = {0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = threadIdx.x + h * kRbThreads;
+    if (b <= E) {
+      // eight chunks at a time: their counts load together
+      constexpr int U = 8;
+      for (int c0 = 0; c0 < nchunks; c0 += U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          v[u] = c0 + u < nchunks ? chunk_hist[(size_t)(c0 + u) * (E + 1) + b] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          tot[h] += v[u];
+          before[h] += c0 + u < (int)blockIdx.x ? v[u] : 0;
+        }
+      }
+    }
+  }
+  // bins 0..255 in thread order, bin 256 after all of them
+  int all;
+  const int excl = rb_block_scan(tot[0], &all, wave_sums);
+  if (threadIdx.x <= E) chunk_start[threadIdx.x] = excl + before[0];
+  if (threadIdx.x == 0 && E >= kRbThreads) chunk_start[kRbThreads] = all + before[1];
+  if (blockIdx.x == 0) {
+    if (threadIdx.x <= E) {
+      counts[threadIdx.x] = tot[0];
+      offsets[threadIdx.x] = excl;
+    }
+    if (threadIdx.x == 0) {
+      if (E >= kRbThreads) {
+        counts[kRbThreads] = tot[1];
+        offsets[kRbThreads] = all;
+      }
+      offsets[E + 1] = R;
+    }
+  }
   __syncthreads();
 
   constexpr int kPerWave = kChunk / kRbWaves;
@@ -128,7 +148,7 @@ __global__ __launch_bounds__(kRbThreads) void rb_scatter_kernel(const int32_t *_
   __syncthreads();
   // per bin: the chunk's base plus the counts of the earlier waves
   for (int b = threadIdx.x; b <= E; b += kRbThreads) {
-    int s = chunk_base[(size_t)blockIdx.x * (E + 1) + b];
+    int s = chunk_start[b];
     for (int v = 0; v < kRbWaves; ++v) {
       const int c = cnt[v][b];
       cnt[v][b] = s;
@@ -248,7 +268,6 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
                               int32_t *route_rows, int32_t *ws, hipStream_t stream) {
   const int nchunks = route_chunks(R);
   int32_t *chunk_hist = ws;
-  int32_t *chunk_base = ws + (size_t)nchunks * (E + 1);
   int key_bits = 1;
   while ((1 << key_bits) < E + 1) ++key_bits;
   if (R <= kFusedMaxR) {
@@ -258,29 +277,28 @@ hipError_t launch_route_build(const int32_t *ids, const uint8_t *mask, int R, in
   }
   hipLaunchKernelGGL(rb_hist_kernel, dim3(nchunks), dim3(kRbThreads), 0, stream, ids, mask, R, E,
                      chunk_hist);
-  hipLaunchKernelGGL(rb_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nchunks,
-                     E, counts, offsets, chunk_base);
   hipLaunchKernelGGL(rb_scatter_kernel, dim3(nchunks), dim3(kRbThreads), 0, stream, ids, mask, R,
-                     E, key_bits, chunk_base, sorted_routes, route_rows);
+                     E, key_bits, nchunks, chunk_hist, counts, offsets, sorted_routes, route_rows);
   return hipGetLastError();
 }
 
 size_t route_build_ws_bytes(int R, int E) {
-  return (size_t)2 * route_chunks(R) * (E + 1) * sizeof(int32_t);
+  return (size_t)route_chunks(R) * (E + 1) * sizeof(int32_t);
 }
 
 // ------------------------------------------------------------------ no allocation
 
-// The route build for callers that cannot allocate: the chunk histograms and
-// chunk bases live in this file-scope device array instead of a caller's
-// workspace.  Each GPU holds its own copy until the process ends; every call
-// on a GPU uses that GPU's copy.  Every word the kernels read there is
-// written earlier in the same call (histograms, then bases), so nothing has
-// to be cleared between calls; calls that overlap on one GPU race.
-static __device__ __align__(256) int32_t scratch[2 * (kRouteNoAllocMaxR / kChunk) * kMaxBins];
+// The route build for callers that cannot allocate: the chunk histograms
+// live in this file-scope device array instead of a caller's workspace.
+// Each GPU holds its own copy until the process ends; every call on a GPU
+// uses that GPU's copy.  Every word the kernels read there is written
+// earlier in the same call (the histogram launch, then the scatter reads),
+// so nothing has to be cleared between calls; calls that overlap on one GPU
+// race.
+static __device__ __align__(256) int32_t scratch[(kRouteNoAllocMaxR / kChunk) * kMaxBins];
 static_assert(kRouteNoAllocMaxR % kChunk == 0, "whole chunks");
-static_assert(sizeof(scratch) >= 2 * (kRouteNoAllocMaxR / kChunk) * (size_t)kMaxBins * 4,
-              "room for the chunk histograms and bases of the largest call");
+static_assert(sizeof(scratch) >= (kRouteNoAllocMaxR / kChunk) * (size_t)kMaxBins * 4,
+              "room for the chunk histograms of the largest call");
 
 namespace {
 constexpr int kMaxDevices = 64;

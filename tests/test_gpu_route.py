@@ -37,9 +37,13 @@ def test_workload_routings(name):
 @pytest.mark.parametrize("T,k,E,p,seed", [
     (1, 1, 1, 0.0, 0), (1, 6, 256, 0.0, 1), (7, 3, 5, 0.3, 2), (21, 3, 256, 0.5, 3),
     (700, 6, 256, 0.05, 4), (20000, 6, 256, 0.05, 5), (4097, 16, 256, 0.2, 6), (333, 2, 2, 0.1, 7),
-    # around the single-workgroup limit (16384 routes) and its 1024-route steps
+    # 1024-route steps of the one-workgroup path and the chunked path
     (1024, 1, 256, 0.1, 8), (1025, 1, 256, 0.1, 9), (4096, 4, 256, 0.05, 10),
     (4097, 4, 256, 0.05, 11), (2731, 6, 100, 0.3, 12),
+    # around the one-workgroup limit (6,144 routes); chunk counts around the
+    # scatter's eight-chunk load groups, few bins, an empty trailing bin
+    (1024, 6, 256, 0.1, 13), (1025, 6, 256, 0.1, 14), (1536, 6, 7, 0.2, 15),
+    (8193, 1, 256, 0.0, 16), (2048, 4, 256, 1.0, 17),
 ])
 def test_random(T, k, E, p, seed):
     rng = np.random.default_rng(seed)
