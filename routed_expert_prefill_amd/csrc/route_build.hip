@@ -1,7 +1,7 @@
 // Route histogram, prefix and stable scatter for up to 256 experts
 // ("perf(ds4): batch heterogeneous MoE prefill by expert", Summary).
 //
-// Up to 6144 routes: one workgroup does all three steps (rb_fused_kernel).
+// Up to 5120 routes: one workgroup does all three steps (rb_fused_kernel).
 // Beyond that, two launches over chunks of kChunk routes:
 //   1. per-chunk histogram in LDS (integer atomics: order-independent);
 //   2. per-chunk stable scatter.  Each workgroup first forms, from all the
@@ -20,17 +20,18 @@ namespace moe {
 
 constexpr int kRbThreads = 256;
 constexpr int kRbWaves = kRbThreads / kWave;
-// Measured on MI355X (route build alone, uniform routing over 256 experts):
-// the one-workgroup path takes 11 us up to ~4k routes, 14 us at 6,144,
-// 19 us at 8,196 and 25 us at 12,288; the chunked path (then three
-// launches, a one-workgroup scan between histogram and scatter) took
-// 16.4-17 us from 8k to 49k routes (1,024-route chunks ~1 us faster than
-// 2,048 at 49k, 512-route chunks 4 us slower).
+// Measured on MI355X (route build alone, uniform routing over 256 experts,
+// calls back to back): the one-workgroup path takes 11 us up to ~4k
+// routes, 14 us at 6,144, 19 us at 8,196 and 25 us at 12,288; the chunked
+// path in two launches 13-14 us from 6 to 49k routes (1,024-route chunks:
+// 512 are ~1 us slower at 49k, 2,048 equal or slower).  The crossing lies
+// between 4,098 routes (one workgroup 2.4 us faster) and 6,144 (0.5 us
+// slower).
 #ifndef MOE_RB_CHUNK
 #define MOE_RB_CHUNK 1024
 #endif
 #ifndef MOE_RB_FUSED_MAX
-#define MOE_RB_FUSED_MAX 6144
+#define MOE_RB_FUSED_MAX 5120
 #endif
 constexpr int kChunk = MOE_RB_CHUNK;  // routes per workgroup
 constexpr int kMaxBins = 257; // E + 1 with E <= 256

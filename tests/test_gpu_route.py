@@ -40,9 +40,10 @@ def test_workload_routings(name):
     # 1024-route steps of the one-workgroup path and the chunked path
     (1024, 1, 256, 0.1, 8), (1025, 1, 256, 0.1, 9), (4096, 4, 256, 0.05, 10),
     (4097, 4, 256, 0.05, 11), (2731, 6, 100, 0.3, 12),
-    # around the one-workgroup limit (6,144 routes); chunk counts around the
+    # around the one-workgroup limit (5,120 routes); chunk counts around the
     # scatter's eight-chunk load groups, few bins, an empty trailing bin
-    (1024, 6, 256, 0.1, 13), (1025, 6, 256, 0.1, 14), (1536, 6, 7, 0.2, 15),
+    (1024, 5, 256, 0.1, 13), (1025, 5, 256, 0.1, 14), (1024, 6, 256, 0.1, 18),
+    (1536, 6, 7, 0.2, 15),
     (8193, 1, 256, 0.0, 16), (2048, 4, 256, 1.0, 17),
 ])
 def test_random(T, k, E, p, seed):
