@@ -168,56 +168,107 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t *_
   }
 }
 
-// Rows of at most kQWaveMaxCols elements: one wave per row (four rows per
-// workgroup), lane l holding elements 8 l + 512 i .. +7 for i < NL, the row
-// maximum reduced with shuffles only.  Same arithmetic as quant_rows_kernel.
+// Rows of at most kQWaveMaxCols elements, one or two waves per row.  A wave
+// holds NL 16-byte loads per lane of its part of the row, columns c0 + 8 l +
+// 512 i .. +7 in lane l; the row maximum is reduced with shuffles (and, for
+// two waves, one exchange through LDS).  Same arithmetic as
+// quant_rows_kernel.
 constexpr int kQWaveMaxCols = 4096;
 
+// loads of one wave's part of a row (columns [c0, min(cols, c0 + NL * 512)))
+// and the wave's maximum magnitude
+template <int NL>
+__device__ __forceinline__ float q_load_part(const uint16_t *row_src, int c0, int cols,
+                                             i32x4 (&raw)[NL]) {
+  const int lane = lane_id();
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int c = c0 + (i * kWave + lane) * 8;  // cols is a multiple of 8
+    if (c < cols) raw[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(row_src + c));
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int c = c0 + (i * kWave + lane) * 8;
+    if (c < cols) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t two = (uint32_t)raw[i][w];
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two & 0xffffu))));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two >> 16))));
+      }
+    }
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  return amax;
+}
+
+// codes of one wave's part of a row, given the row maximum
+template <int NL>
+__device__ __forceinline__ void q_store_part(uint8_t *row_dst, int c0, int cols,
+                                             const i32x4 (&raw)[NL], float amax) {
+  const int lane = lane_id();
+  const bool zero = amax == 0.0f;
+  const float sc = zero ? 1.0f : amax / 448.0f;
+  bool exact;
+  const float rcp = quant_rcp(sc, &exact);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int c = c0 + (i * kWave + lane) * 8;
+    if (c < cols) {
+      uint2 out;
+      out.x = quant_e4m3_x4((uint32_t)raw[i][0], (uint32_t)raw[i][1], sc, rcp, exact, zero);
+      out.y = quant_e4m3_x4((uint32_t)raw[i][2], (uint32_t)raw[i][3], sc, rcp, exact, zero);
+      *reinterpret_cast<uint2 *>(row_dst + c) = out;
+    }
+  }
+}
+
+__device__ __forceinline__ float q_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+// one wave per row, four rows per workgroup
 template <int NL>
 __global__ __launch_bounds__(kQThreads) void quant_rows_wave_kernel(
     const uint16_t *__restrict__ x, int rows, const int32_t *rows_dev, int cols,
     uint8_t *__restrict__ q, float *__restrict__ s) {
   const int nrows = rows_dev ? *rows_dev : rows;
-  const int lane = lane_id();
   const int waves = gridDim.x * (kQThreads / kWave);
   for (int row = blockIdx.x * (kQThreads / kWave) + threadIdx.x / kWave; row < nrows; row += waves) {
-    const uint16_t *src = x + (size_t)row * cols;
     i32x4 raw[NL];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = (i * kWave + lane) * 8;  // cols is a multiple of 8
-      if (c < cols) raw[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + c));
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = (i * kWave + lane) * 8;
-      if (c < cols) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t two = (uint32_t)raw[i][w];
-          amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two & 0xffffu))));
-          amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(two >> 16))));
-        }
-      }
-    }
-    for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const bool zero = amax == 0.0f;
-    const float sc = zero ? 1.0f : amax / 448.0f;
-    bool exact;
-    const float rcp = quant_rcp(sc, &exact);
-    if (lane == 0) s[row] = sc;
-    uint8_t *dst = q + (size_t)row * cols;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = (i * kWave + lane) * 8;
-      if (c < cols) {
-        uint2 out;
-        out.x = quant_e4m3_x4((uint32_t)raw[i][0], (uint32_t)raw[i][1], sc, rcp, exact, zero);
-        out.y = quant_e4m3_x4((uint32_t)raw[i][2], (uint32_t)raw[i][3], sc, rcp, exact, zero);
-        *reinterpret_cast<uint2 *>(dst + c) = out;
-      }
-    }
+    const float amax = q_load_part<NL>(x + (size_t)row * cols, 0, cols, raw);
+    if (lane_id() == 0) s[row] = q_scale(amax);
+    q_store_part<NL>(q + (size_t)row * cols, 0, cols, raw, amax);
+  }
+}
+
+// two waves per row (columns [0, NL * 512) and the rest), two rows per
+// workgroup: for 4096-column rows the registers of one wave's half keep the
+// kernel at twice the occupancy of a whole row per wave (MI355X, 8192 x 4096:
+// 44 -> 36 us)
+template <int NL>
+__global__ __launch_bounds__(kQThreads) void quant_rows_pair_kernel(
+    const uint16_t *__restrict__ x, int rows, const int32_t *rows_dev, int cols,
+    uint8_t *__restrict__ q, float *__restrict__ s) {
+  constexpr int kRowsPerBlock = kQThreads / kWave / 2;
+  __shared__ float part[2][kQThreads / kWave];  // per wave, double-buffered by trip
+  const int nrows = rows_dev ? *rows_dev : rows;
+  const int wave = threadIdx.x / kWave;
+  const int c0 = (wave & 1) * NL * kWave * 8;
+  int trip = 0;
+  // the trip count is the same for every wave of the workgroup, so all of
+  // them meet each barrier
+  for (int base = blockIdx.x * kRowsPerBlock; base < nrows;
+       base += gridDim.x * kRowsPerBlock, trip ^= 1) {
+    const int row = base + wave / 2;
+    const bool on = row < nrows;
+    i32x4 raw[NL];
+    float amax = on ? q_load_part<NL>(x + (size_t)row * cols, c0, cols, raw) : 0.0f;
+    if (lane_id() == 0) part[trip][wave] = amax;
+    __syncthreads();
+    amax = fmaxf(amax, part[trip][wave ^ 1]);
+    if (!on) continue;
+    if (lane_id() == 0 && c0 == 0) s[row] = q_scale(amax);
+    q_store_part<NL>(q + (size_t)row * cols, c0, cols, raw, amax);
   }
 }
 
@@ -226,21 +277,21 @@ int quant_max_cols() { return kQMaxCols; }
 hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream) {
   if (cols <= kQWaveMaxCols) {
-    const int per_block = kQThreads / kWave;
+    const int nl = (cols + kWave * 8 - 1) / (kWave * 8);
+    const int per_block = nl <= 4 ? kQThreads / kWave : kQThreads / kWave / 2;
     const long long want = ((long long)rows + per_block - 1) / per_block;
     // up to 16 workgroups per CU (four times grid_cap): more rows in flight
     // at once (MI355X, 46,700 x 2048: 4 per CU 106 us, 16 per CU 80 us)
     const long long cap = (long long)grid_cap * 4;
     const int grid = (int)(want < cap ? want : cap);
-    const int nl = (cols + kWave * 8 - 1) / (kWave * 8);
     if (nl <= 2)
       hipLaunchKernelGGL(quant_rows_wave_kernel<2>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
                          stream, x, rows, rows_dev, cols, q, s);
     else if (nl <= 4)
       hipLaunchKernelGGL(quant_rows_wave_kernel<4>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
                          stream, x, rows, rows_dev, cols, q, s);
-    else
-      hipLaunchKernelGGL(quant_rows_wave_kernel<8>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+    else  // up to 4096 columns: two waves of four loads per lane
+      hipLaunchKernelGGL(quant_rows_pair_kernel<4>, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
                          stream, x, rows, rows_dev, cols, q, s);
     return hipGetLastError();
   }
