@@ -426,15 +426,17 @@ struct GgDispatch {
     nbig = vreg(*a.ntiles) - nsmall;
     // weight rows per item of the taller tiles (wrb) and of the 32-row tiles
     // (wrs).  Left to the device (0), 32-row tiles take 128-row items when
-    // there are no taller tiles: on MI355X at 401 tokens (every expert under
+    // there are no taller tiles (or few, below): on MI355X at 401 tokens (every expert under
     // 32 rows) gate/up 1.349 -> 1.313 ms and down 0.703 -> 0.687 ms, one
     // expert owner's share 0.348 -> 0.320 ms per step: twice the items to
     // balance, and a 20 KB stage leaves eight ring slots where a 36 KB one
     // leaves four.
     const int wr = vreg(a.wr);
-    // (also narrowing the 32-row tiles of mixed lists: 2048 tokens -1%,
-    // 8192 Zipf-routed tokens +4%, so not done)
-    const bool narrow = wr == 0 && nbig == 0;
+    // Mixed lists narrow their 32-row tiles too while the tiles of experts
+    // with several tiles are under an eighth of the list (2048 tokens:
+    // 2.295 -> 2.267 ms per step); with many of those (8192 Zipf-routed
+    // tokens) narrowing cost 4%, with few it changes nothing there.
+    const bool narrow = wr == 0 && (nbig == 0 || vreg(*a.n_multi) * 8 < vreg(*a.ntiles));
     wrb = wr == 0 ? kGgWRows : wr;
     wrs = narrow ? kGgWRows / 2 : wrb;
     // output features per block: half the weight rows for gate/up (gate and
@@ -453,8 +455,9 @@ struct GgDispatch {
     // than the workgroups (MI355X: one expert owner's share, 32 tiles, down
     // 0.106 -> 0.102 ms; 16 tokens 0.636 -> 0.619 ms, 32 tokens 1.054 ->
     // 1.037 ms per step); with a tile per workgroup or more one block is
-    // best (401 tokens, 256 tiles: down 0.689 ms, 0.715 with two, 0.699 with four)
-    if (narrow && !GATEUP && nsmall < grid && N % (4 * FEATS) == 0) nbs = 4;
+    // best (401 tokens, 256 tiles: down 0.689 ms, 0.715 with two, 0.699 with
+    // four); in mixed lists one block (2048 tokens: down 0.801 -> 0.793 ms)
+    if (narrow && nbig == 0 && !GATEUP && nsmall < grid && N % (4 * FEATS) == 0) nbs = 4;
     // with few tiles, halve the blocks per item until at least half the
     // workgroups have an item: a workgroup of a half-idle chip streams faster
     // than its even share, so long items on half of them still pay (measured:
