@@ -190,6 +190,11 @@ int moe_grouped_ffn(const moe_ffn_desc *desc /* host */, const void *x, const in
  * moe_ffn_down     (fp8: quantises h per row) down GEMM -> y.
  * Arguments mean what they mean for moe_grouped_ffn; unused ones may be NULL
  * (x is used by plan only in fp8 mode).  Errors as for moe_grouped_ffn.
+ * After one plan, moe_ffn_gate_up and moe_ffn_down may each run again (for
+ * instance for timing): the GEMM kernels leave their work-queue state in
+ * the workspace as the plan left it.  A new offsets array needs a new plan.
+ * The stage calls issue no memset and allocate nothing, so a sequence of
+ * them (or of moe_grouped_ffn) can be captured in a HIP graph and replayed.
  */
 int moe_ffn_plan(const moe_ffn_desc *desc /* host */, const void *x, const int32_t *offsets,
                  void *workspace, size_t workspace_bytes, moe_stream_t stream);
