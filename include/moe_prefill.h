@@ -186,8 +186,9 @@ int moe_grouped_ffn(const moe_ffn_desc *desc /* host */, const void *x, const in
  *
  * moe_ffn_plan     builds the tile schedule from offsets (device work list of
  *                  expert row tiles; fp8: also quantises x into the workspace).
- * moe_ffn_gate_up  gate/up GEMM with SwiGLU fused into the epilogue -> h.
- * moe_ffn_down     (fp8: quantises h per row) down GEMM -> y.
+ * moe_ffn_gate_up  gate/up GEMM with SwiGLU fused into the epilogue -> h
+ *                  (fp8: the epilogue also keeps each row's max |h|).
+ * moe_ffn_down     (fp8: quantises h per row with those maxima) down GEMM -> y.
  * Arguments mean what they mean for moe_grouped_ffn; unused ones may be NULL
  * (x is used by plan only in fp8 mode).  Errors as for moe_grouped_ffn.
  * After one plan, moe_ffn_gate_up and moe_ffn_down may each run again (for

@@ -38,7 +38,7 @@ int num_cus_current_device() {
 int grid_cap_for_current_device() { return num_cus_current_device() * 4; }
 
 struct FfnLayout {
-  size_t sched, tiles, h, qx, sx, qh, sh, total;
+  size_t sched, tiles, h, qx, sx, qh, sh, hmax, total;
 };
 
 bool ffn_desc_status(const moe_ffn_desc *d, int *st) {
@@ -94,6 +94,8 @@ FfnLayout ffn_layout(const moe_ffn_desc *d) {
     L.qh = off;
     off += align_up(R * (size_t)d->f);
     L.sh = off;
+    off += align_up(R * 4);
+    L.hmax = off;  // row maxima of |h|, kept by the gate/up epilogue
     off += align_up(R * 4);
   }
   L.total = off;
@@ -232,6 +234,7 @@ int ffn_call(const moe_ffn_desc *desc, int stages, const void *x, const int32_t 
   L.h = reinterpret_cast<uint16_t *>(ws + lay.h);
   L.qh = reinterpret_cast<uint8_t *>(ws + lay.qh);
   L.sh = reinterpret_cast<float *>(ws + lay.sh);
+  L.hmax = reinterpret_cast<uint32_t *>(ws + lay.hmax);
   L.sch = reinterpret_cast<moe::Schedule *>(ws + lay.sched);
   L.tiles = reinterpret_cast<moe::Tile *>(ws + lay.tiles);
   L.num_cus = num_cus_current_device();

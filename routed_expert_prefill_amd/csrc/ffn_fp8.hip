@@ -12,7 +12,8 @@
 // in 16-row groups; down: one to four blocks of 128 features streamed
 // through one ring fill), which keeps the fold of a wave in proportion to
 // its MFMAs; 192-row tiles have a layout of their own.  Between the
-// projections h is written in bf16 and then quantised per row.
+// projections h is written in bf16, the gate/up epilogue keeps each row's
+// max |h| (atomicMax), and the down stage quantises h per row with it.
 #include "kernels.h"
 #include "ring.h"
 
@@ -33,6 +34,7 @@ struct Gg8Args {
   int *counter;        // compute-queue head (TwoQueue)
   int *counter_s;      // stream-queue head
   int nb;  // feature blocks per item (streamed through one ring fill)
+  uint32_t *hmax;  // gate/up: [R] fp32 bits of max |h| per row, kept with atomicMax
 };
 
 constexpr int kG8Threads = 512;
@@ -256,6 +258,7 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
       if (row < t.nrows) {
         const int i = t.row0 + row;
         const float rs = rsc[tt];
+        uint32_t hm = 0;  // gate/up: max |h| of this lane's values of row i, as bf16 bits
 #pragma unroll
         for (int tw = 0; tw < TW; ++tw) {
           const int wt = L::wtile(wv, tw);
@@ -265,11 +268,16 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
             for (int g = 0; g < 2; ++g) {
               const f32x4 gv = quad_scaled(acc[tw][tt], g, rs);
               const f32x4 uv = quad_scaled(acc[tw][tt], g + 2, rs);
+              uint32_t hb[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                hb[e] = f32_to_bf16_bits(swiglu(gv[e], uv[e]));
+                const uint32_t ab = hb[e] & 0x7fffu;
+                hm = ab <= 0x7f80u && ab > hm ? ab : hm;  // NaN left out
+              }
               uint2 v;
-              v.x = (uint32_t)f32_to_bf16_bits(swiglu(gv[0], uv[0])) |
-                    ((uint32_t)f32_to_bf16_bits(swiglu(gv[1], uv[1])) << 16);
-              v.y = (uint32_t)f32_to_bf16_bits(swiglu(gv[2], uv[2])) |
-                    ((uint32_t)f32_to_bf16_bits(swiglu(gv[3], uv[3])) << 16);
+              v.x = hb[0] | (hb[1] << 16);
+              v.y = hb[2] | (hb[3] << 16);
               const int n = nb0 + wt * 16 + g * 8 + rh * 4;
               *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)i * a.N + n) = v;
             }
@@ -282,6 +290,14 @@ __device__ __forceinline__ void g8_item(const Gg8Args &a, const Tile &t, int n0,
                     quad_scaled(acc[tw][tt], g, rs);
             }
           }
+        }
+        if (GATEUP) {
+          // the row's maximum over this wave: lanes rr and rr + 32 hold the
+          // same row; one atomic per row and wave (fp32 bits of a
+          // non-negative value order like the values)
+          const uint32_t other = (uint32_t)__shfl_xor((int)hm, 32);
+          hm = other > hm ? other : hm;
+          if (rh == 0) atomicMax(a.hmax + i, hm << 16);
         }
       }
     }
@@ -429,6 +445,8 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     if (err != hipSuccess) return err;
     err = launch_quant_rows(L.x, L.T, nullptr, L.d, L.qx, L.sx, L.grid_cap, stream);
     if (err != hipSuccess) return err;
+    err = launch_zero_u32(L.hmax, L.R, stream);  // the gate/up epilogue maxes into it
+    if (err != hipSuccess) return err;
   }
   Gg8Args g{};
   g.k = L.k;
@@ -449,15 +467,19 @@ hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream)
     g.counter = &L.sch->counter[0];
     g.counter_s = &L.sch->counter_s[0];
     g.nb = 1;
+    g.hmax = L.hmax;
     hipLaunchKernelGGL(grouped_gemm8_kernel<true>, dim3(L.num_cus), dim3(kG8Threads), 0, stream,
                        g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (stages & kStageDown) {
-    // h -> per-row E4M3; the active row count is offsets[E]
-    err = launch_quant_rows(L.h, L.R, L.offsets + L.E, L.f, L.qh, L.sh, L.grid_cap, stream);
+    // h -> per-row E4M3 with the row maxima the gate/up epilogue kept; the
+    // active row count is offsets[E]
+    err = launch_quant_rows_known_max(L.h, L.R, L.offsets + L.E, L.f, L.hmax, L.qh, L.sh,
+                                      L.grid_cap, stream);
     if (err != hipSuccess) return err;
+    g.hmax = nullptr;
     g.act = L.qh;
     g.act_scale = L.sh;
     g.sorted_routes = nullptr;

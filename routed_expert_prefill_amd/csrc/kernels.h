@@ -58,8 +58,9 @@ struct FfnLaunch {
 };
 hipError_t launch_grouped_ffn_bf16(const FfnLaunch &L, int stages, hipStream_t stream);
 
-// fp8 grouped FFN: plan (schedule + per-row quantisation of x into qx, sx),
-// gate/up + SwiGLU (h in bf16), down (per-row quantisation of h, then GEMM).
+// fp8 grouped FFN: plan (schedule, per-row quantisation of x into qx, sx,
+// row maxima of h cleared), gate/up + SwiGLU (h in bf16, its row maxima
+// kept), down (per-row quantisation of h with those maxima, then GEMM).
 struct FfnLaunchFp8 {
   const uint16_t *x;
   uint8_t *qx;
@@ -72,6 +73,7 @@ struct FfnLaunchFp8 {
   uint16_t *h;
   uint8_t *qh;
   float *sh;
+  uint32_t *hmax;  // [R] bits of max |h| per row (the gate/up epilogue keeps them)
   Schedule *sch;
   Tile *tiles;
   int T, k, E, d, f, R;
@@ -79,5 +81,14 @@ struct FfnLaunchFp8 {
   int num_cus;
 };
 hipError_t launch_ffn_fp8(const FfnLaunchFp8 &L, int stages, hipStream_t stream);
+
+// Per-row E4M3 quantisation of bf16 rows whose maxima are known: amax_bits[r]
+// holds the fp32 bits of max |x[r, :]|; same codes and scales as
+// launch_quant_rows.  rows_dev as there.
+hipError_t launch_quant_rows_known_max(const uint16_t *x, int rows, const int32_t *rows_dev,
+                                       int cols, const uint32_t *amax_bits, uint8_t *q, float *s,
+                                       int grid_cap, hipStream_t stream);
+// zero n 32-bit words (a kernel, not a memset: the path stays graph-capturable)
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t stream);
 
 }  // namespace moe

@@ -272,7 +272,59 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_pair_kernel(
   }
 }
 
+// Rows whose maxima are known (amax_bits[r] = fp32 bits of max |x[r, :]|,
+// NaN elements left out, as fmaxf does above): no reduction, so every
+// thread encodes 8 consecutive elements of any row, 16-byte non-temporal
+// loads and 8-byte stores, the row's scale written by the thread of its
+// first 8 elements.  Same scale and codes as the kernels above.
+__global__ __launch_bounds__(kQThreads) void quant_rows_known_max_kernel(
+    const uint16_t *__restrict__ x, int rows, const int32_t *rows_dev, int cols,
+    const uint32_t *__restrict__ amax_bits, uint8_t *__restrict__ q, float *__restrict__ s) {
+  const int nrows = rows_dev ? *rows_dev : rows;
+  const int per_row = cols / 8;  // cols is a multiple of 8
+  const long long n = (long long)nrows * per_row;
+  for (long long c = (long long)blockIdx.x * kQThreads + threadIdx.x; c < n;
+       c += (long long)gridDim.x * kQThreads) {
+    const int row = (int)(c / per_row);
+    const int col = (int)(c - (long long)row * per_row) * 8;
+    const float amax = __uint_as_float(amax_bits[row]);
+    const bool zero = amax == 0.0f;
+    const float sc = q_scale(amax);
+    bool exact;
+    const float rcp = quant_rcp(sc, &exact);
+    const size_t o = (size_t)row * cols + col;
+    const i32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(x + o));
+    uint2 out;
+    out.x = quant_e4m3_x4((uint32_t)raw[0], (uint32_t)raw[1], sc, rcp, exact, zero);
+    out.y = quant_e4m3_x4((uint32_t)raw[2], (uint32_t)raw[3], sc, rcp, exact, zero);
+    *reinterpret_cast<uint2 *>(q + o) = out;
+    if (col == 0) s[row] = sc;
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void zero_u32_kernel(uint32_t *__restrict__ p, int n) {
+  for (int i = blockIdx.x * kQThreads + threadIdx.x; i < n; i += gridDim.x * kQThreads) p[i] = 0u;
+}
+
 int quant_max_cols() { return kQMaxCols; }
+
+hipError_t launch_quant_rows_known_max(const uint16_t *x, int rows, const int32_t *rows_dev,
+                                       int cols, const uint32_t *amax_bits, uint8_t *q, float *s,
+                                       int grid_cap, hipStream_t stream) {
+  const long long chunks = (long long)rows * (cols / 8);
+  const long long want = (chunks + kQThreads - 1) / kQThreads;
+  const long long cap = (long long)grid_cap * 4;
+  const int grid = (int)(want < cap ? want : cap);
+  hipLaunchKernelGGL(quant_rows_known_max_kernel, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0,
+                     stream, x, rows, rows_dev, cols, amax_bits, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t stream) {
+  const int grid = (n + kQThreads * 4 - 1) / (kQThreads * 4);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(grid > 0 ? grid : 1), dim3(kQThreads), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const uint16_t *x, int rows, const int32_t *rows_dev, int cols,
                              uint8_t *q, float *s, int grid_cap, hipStream_t stream) {
